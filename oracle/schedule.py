@@ -1,0 +1,83 @@
+"""Reference split-KV work schedule (the metadata step), in plain Python loops.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Role, from "矩阵、注意力与 GPU：拆解 DeepGEMM 与 FlashMLA" (msy.plus) §七
+"split-KV：把长序列切开": a metadata call, made once per decode step and
+reused by every layer, states which sequences, which KV blocks and how many
+splits each processor part takes. The pages give no format or balancing rule,
+so this is the library's own documented rule, written here as a per-tile
+assignment (the GPU computes the same result per part, in parallel):
+
+  * Work units are "row-group sequences" q = b * n_rg + rg, rg = i * n_hb + hb
+    (query position i, head block hb of rg_rows heads). Unit q has T_q tiles
+    of 64 tokens: ceil(L_b / 64) dense, ceil(topk / 64) sparse.
+  * Units are laid end to end on a line; a non-empty unit first takes
+    fixed_cost positions (its per-split overhead), then one position per tile.
+  * With total = sum over non-empty units of (fixed_cost + T_q) and
+    W = max(ceil(total / num_parts), min_payload), the tile at position x
+    belongs to part floor(x / W).
+  * A unit's splits are the distinct parts among its tiles, in order.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK_SIZE = 64
+
+
+def tile_counts(cache_seqlens: Optional[Sequence[int]], batch: int, s_q: int, h_q: int,
+                topk: int, rg_rows: int) -> List[int]:
+    """T_q for every row-group sequence, in q order."""
+    n_hb = -(-h_q // rg_rows)
+    n_rg = s_q * n_hb
+    out = []
+    for b in range(batch):
+        T = -(-topk // BLOCK_SIZE) if topk > 0 else -(-max(int(cache_seqlens[b]), 0) // BLOCK_SIZE)
+        out.extend([T] * n_rg)
+    return out
+
+
+def split_schedule(T: Sequence[int], num_parts: int, fixed_cost: int, min_payload: int
+                   ) -> Tuple[np.ndarray, np.ndarray]:
+    """Returns (tile_meta int32 [num_parts, 8], split_offsets int32 [Q + 1]).
+
+    tile_meta[p] = [q_begin, t_begin, q_end, t_end (inclusive), first_split,
+                    empty (1/0), 0, 0]; an empty part has all zeros but the
+    empty flag. split_offsets is the prefix sum of per-unit split counts.
+    """
+    total = sum(fixed_cost + t for t in T if t > 0)
+    W = max(-(-total // num_parts) if total > 0 else 1, min_payload, 1)
+    owner: Dict[Tuple[int, int], int] = {}
+    pos = 0
+    for q, t_count in enumerate(T):
+        if t_count <= 0:
+            continue
+        pos += fixed_cost
+        for t in range(t_count):
+            owner[(q, t)] = pos // W
+            pos += 1
+    parts: List[List[Tuple[int, int]]] = [[] for _ in range(num_parts)]
+    for (q, t), p in owner.items():  # dict keeps insertion (q, t) order
+        assert p < num_parts
+        parts[p].append((q, t))
+    n_splits = [0] * len(T)
+    for q, t_count in enumerate(T):
+        if t_count > 0:
+            n_splits[q] = len({owner[(q, t)] for t in range(t_count)})
+    split_offsets = np.zeros(len(T) + 1, dtype=np.int32)
+    split_offsets[1:] = np.cumsum(n_splits)
+    meta = np.zeros((num_parts, 8), dtype=np.int32)
+    for p, tiles in enumerate(parts):
+        if not tiles:
+            meta[p, 5] = 1
+            continue
+        qb, tb = tiles[0]
+        qe, te = tiles[-1]
+        first_split = len({owner[(qb, t)] for t in range(tb)})
+        meta[p, :6] = [qb, tb, qe, te, first_split, 0]
+    return meta, split_offsets

@@ -1,0 +1,129 @@
+"""Plant plausible mistakes in the oracle (CPU, monkeypatched) and check that
+the pins catch each one. This guards the pins themselves: a pin that passes
+on a broken oracle would prove nothing."""
+
+import numpy as np
+import pytest
+
+import oracle.mla_oracle as om
+import tests.test_oracle_attention as ta
+import tests.test_oracle_formats as tf
+
+
+def _attend_no_rope(q, K, scale):
+    if K.shape[0] == 0:
+        return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
+    S = (q[:, :512] @ K[:, :512].T) * scale
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ K[:, :512], (m + np.log(l))[:, 0]
+
+
+def _attend_wrong_value_slice(q, K, scale):
+    if K.shape[0] == 0:
+        return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
+    S = (q @ K.T) * scale
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ K[:, 64:], (m + np.log(l))[:, 0]
+
+
+def _attend_lse_without_max(q, K, scale):
+    if K.shape[0] == 0:
+        return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
+    S = (q @ K.T) * scale
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ K[:, :512], np.log(l)[:, 0]
+
+
+_real_attended_rows = om.attended_rows
+
+
+def _rows_causal_off_by_one(b, i, *, s_q, num_rows, block_table, cache_seqlens, causal, indices):
+    if causal and indices is None:
+        L = int(cache_seqlens[b])
+        t = np.arange(max(0, L - s_q + i))
+        return np.asarray(block_table[b])[t // 64] * 64 + t % 64
+    return _real_attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
+                               cache_seqlens=cache_seqlens, causal=causal, indices=indices)
+
+
+def _rows_ignore_block_table(b, i, *, s_q, num_rows, block_table, cache_seqlens, causal, indices):
+    if indices is None:
+        return np.arange(int(cache_seqlens[b]))
+    return _real_attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
+                               cache_seqlens=cache_seqlens, causal=causal, indices=indices)
+
+
+def _rows_keep_minus_one(b, i, *, s_q, num_rows, block_table, cache_seqlens, causal, indices):
+    if indices is not None:
+        idx = np.asarray(indices[b, i], dtype=np.int64)
+        return idx[idx < num_rows]  # forgets to drop -1 (reads the last row)
+    return _real_attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
+                               cache_seqlens=cache_seqlens, causal=causal, indices=indices)
+
+
+_real_decode = om.decode_rows
+
+
+def _decode_scale_per_64(rows, kv_format):
+    out = _real_decode(rows, kv_format)
+    if kv_format != "fp8":
+        return out
+    n = rows.shape[0]
+    codes = om.E4M3FN_VALUES[rows[:, :512]].astype(np.float32)
+    scales = rows[:, 512:528].copy().view("<f4").reshape(n, 4)
+    sc = np.repeat(np.tile(scales, 2), 64, axis=1).astype(np.float32)  # wrong group width
+    out[:, :512] = om.bf16_bits_to_f64(om.f32_to_bf16_bits(codes * sc))
+    return out
+
+
+def _bf16_truncate(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+ATTENTION_PINS = [
+    ta.test_absorbed_equals_unabsorbed_mha,
+    ta.test_single_token_returns_its_latent,
+    ta.test_equal_scores_give_mean_of_latents,
+    ta.test_split_merge_identity,
+    ta.test_causal_alignment,
+    ta.test_page_permutation_invariance,
+    ta.test_sparse_all_rows_equals_dense_and_ignores_invalid,
+]
+
+
+@pytest.mark.parametrize("mutant", [_attend_no_rope, _attend_wrong_value_slice, _attend_lse_without_max])
+def test_attend_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(om, "attend", mutant)
+    monkeypatch.setattr(ta, "attend", mutant)
+    assert any(_fails(p) for p in ATTENTION_PINS)
+
+
+@pytest.mark.parametrize("mutant", [_rows_causal_off_by_one, _rows_ignore_block_table, _rows_keep_minus_one])
+def test_masking_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(om, "attended_rows", mutant)
+    assert any(_fails(p) for p in ATTENTION_PINS)
+
+
+def test_fp8_group_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(om, "decode_rows", _decode_scale_per_64)
+    monkeypatch.setattr(tf, "decode_rows", _decode_scale_per_64)
+    assert _fails(tf.test_fp8_decode_within_quantisation_bound) or _fails(tf.test_fp8_row_golden)
+
+
+def test_bf16_rounding_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(tf, "f32_to_bf16_bits", _bf16_truncate)
+    assert _fails(tf.test_bf16_rne_matches_torch)

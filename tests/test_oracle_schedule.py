@@ -1,0 +1,74 @@
+"""Pins for the reference split schedule (CPU only): hand-worked cases and invariants."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import split_schedule, tile_counts
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_worked_cases():
+    with open(os.path.join(GOLDEN, "schedule_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        meta, offs = split_schedule(c["T"], c["num_parts"], c["fixed_cost"], c["min_payload"])
+        assert meta.tolist() == c["tile_meta"], c["worked"]
+        assert offs.tolist() == c["split_offsets"], c["worked"]
+
+
+def _expand(meta, T):
+    """All (q, t) tiles of each part, walking q in order from its begin to its end."""
+    out = []
+    for row in meta:
+        qb, tb, qe, te, fs, empty = row[:6]
+        tiles = []
+        if not empty:
+            for q in range(qb, qe + 1):
+                t0 = tb if q == qb else 0
+                t1 = te if q == qe else T[q] - 1
+                tiles += [(q, t) for t in range(t0, t1 + 1)]
+        out.append(tiles)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    Q = int(rng.integers(1, 40))
+    T = [int(x) for x in rng.integers(0, 50, Q)]
+    if seed % 5 == 0:
+        T[int(rng.integers(0, Q))] = 0
+    P = int(rng.choice([1, 3, 8, 64, 256]))
+    C = int(rng.integers(0, 5))
+    Wmin = int(rng.integers(1, 8))
+    meta, offs = split_schedule(T, P, C, Wmin)
+    parts = _expand(meta, T)
+    seen = [t for p in parts for t in p]
+    # every tile exactly once, in (q, t) order across parts
+    assert seen == [(q, t) for q in range(Q) for t in range(T[q])]
+    # split counts and first_split agree with the parts
+    n_splits = np.diff(offs)
+    for q in range(Q):
+        owners = [p for p, tiles in enumerate(parts) if any(x[0] == q for x in tiles)]
+        assert n_splits[q] == len(owners)
+        for k, p in enumerate(owners):
+            if parts[p][0][0] == q:
+                assert meta[p][4] == k
+    # balance: no part holds more than W positions (tiles plus overheads it starts)
+    total = sum(C + t for t in T if t > 0)
+    W = max(-(-total // P) if total else 1, Wmin)
+    for tiles in parts:
+        assert len(tiles) <= W
+
+
+def test_tile_counts_layout():
+    # h_q = 128 with 128-row groups, s_q = 2: two row groups per batch entry
+    assert tile_counts([64, 65, 0], 3, 2, 128, 0, 128) == [1, 1, 2, 2, 0, 0]
+    # h_q = 20 with 16-row groups: two head blocks
+    assert tile_counts([130], 1, 1, 20, 0, 16) == [3, 3]
+    # sparse ignores cache_seqlens
+    assert tile_counts([5, 5], 2, 1, 128, 2048, 128) == [32, 32]
