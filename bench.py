@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""MLA decode throughput on one MI355X.
+
+A step is one pass of the whole decode path over one batch: the split
+schedule (metadata kernel), the split decode kernel, and the split merge
+(combine kernel). Steps run from a HIP graph over rotating copies of the
+inputs whose combined size exceeds 512 MB, so the 256 MB Infinity Cache does
+not serve the KV reads. Inputs are resident in HBM before timing starts.
+
+Default workload: dense bf16 decode, B=16, s_q=1, h_q=128, sequence lengths
+drawn uniformly from [1024, 4096] (seed 0), 64-token pages with a shuffled
+block table. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FLOP_PER_PAIR = 2 * (576 + 512)  # QK^T over 576 dims + PV over 512 dims, per (query row, token)
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MLA decode TFLOPS and KV-read GB/s (% of MI355X roofline) vs seqlen, 1 GPU"
+
+
+def algorithmic_counts(w):
+    """(unmasked (row, token) pairs, KV bytes read once per sequence)."""
+    import numpy as np
+
+    row_bytes = 1152 if w.kv_format == "bf16" else 656
+    if w.indices is not None:
+        idx = w.indices.numpy()
+        valid = (idx >= 0) & (idx < w.num_blocks * 64)
+        pairs = int(valid.sum()) * w.h_q
+        # KV bytes: distinct rows attended per (b) -- each row read once per sequence
+        kv_rows = 0
+        for b in range(w.batch):
+            kv_rows += len(np.unique(idx[b][valid[b]]))
+        return pairs, kv_rows * row_bytes
+    L = w.cache_seqlens.numpy().astype(np.int64)
+    pairs = 0
+    for i in range(w.s_q):
+        lim = np.clip(L - w.s_q + 1 + i, 0, None) if w.causal else L
+        pairs += int(lim.sum()) * w.h_q
+    return pairs, int(L.sum()) * row_bytes
+
+
+def build_workload(args):
+    from workload import config_workload
+
+    return config_workload(args.config, seqlen=args.seqlen)
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the float64 oracle on the host cores over a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla_decode_ref
+
+    q = w.q.view(torch.int16).numpy().view(np.uint16)
+    bt = None if w.block_table is None else w.block_table.numpy()
+    idx = None if w.indices is None else w.indices.numpy()
+    kv = w.kv.numpy()
+    seq = w.cache_seqlens.numpy()
+    rows = [(b, i) for b in range(w.batch) for i in range(w.s_q)]
+    # FLOPs per (b, i) row
+    def row_pairs(b, i):
+        if idx is not None:
+            v = idx[b, i]
+            return int(((v >= 0) & (v < w.num_blocks * 64)).sum()) * w.h_q
+        L = int(seq[b])
+        lim = max(0, L - w.s_q + 1 + i) if w.causal else L
+        return lim * w.h_q
+
+    done_pairs = 0
+    n_rows = 0
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds and k < 10 * len(rows):
+        b, i = rows[k % len(rows)]
+        mla_decode_ref(q, kv, w.kv_format, block_table=bt, cache_seqlens=seq, softmax_scale=w.softmax_scale,
+                       causal=w.causal, indices=idx, rows=[(b, i)])
+        done_pairs += row_pairs(b, i)
+        n_rows += 1
+        k += 1
+    dt = time.perf_counter() - t0
+    threads = max([x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
+    return {
+        "value": done_pairs * FLOP_PER_PAIR / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n_rows} (batch, query-position) rows of the same workload, float64 NumPy, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: dense bf16 h_q=128)")
+    ap.add_argument("--seqlen", type=int, default=65536, help="sequence length for workload 3")
+    ap.add_argument("--num-parts", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_latent_kv_10_amd as mla
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = build_workload(args)
+    pairs, kv_bytes = algorithmic_counts(w)
+    flops = pairs * FLOP_PER_PAIR
+    num_parts = args.num_parts or mla.default_num_parts(0)
+
+    # rotating input copies: touched bytes per step x sets > 512 MB
+    q_bytes = w.q.numel() * 2
+    touched = kv_bytes + 2 * q_bytes
+    n_sets = max(1, math.ceil(512e6 / max(touched, 1)) + 1)
+    sets = []
+    base = {
+        "q": w.q.to(dev), "kv": w.kv.to(dev),
+        "bt": None if w.block_table is None else w.block_table.to(dev),
+        "seq": w.cache_seqlens.to(dev),
+        "idx": None if w.indices is None else w.indices.to(dev),
+    }
+    is_fp8 = w.kv_format == "fp8"
+    n_meta, n_off = mla.metadata_size(w.batch, w.s_q, w.h_q, num_parts)
+    ws_bytes = mla.workspace_size(w.batch, w.s_q, w.h_q, num_parts)
+    for s in range(n_sets):
+        d = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
+        d["tm"] = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+        d["so"] = torch.empty((n_off,), dtype=torch.int32, device=dev)
+        d["ws"] = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        d["o"] = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+        d["lse"] = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+        d["args"] = mla.make_args(d["q"], d["kv"], d["bt"], d["seq"], d["tm"], d["so"], w.softmax_scale, w.causal,
+                                  is_fp8, d["idx"], d["ws"], d["o"], d["lse"])
+        sets.append(d)
+    L = mla.lib()
+    import ctypes
+
+    def step(d, stream, with_decode=True):
+        sp = 0 if d["idx"] is not None else d["seq"].data_ptr()
+        mla.check(L.mla_get_metadata(sp, w.batch, w.s_q, w.h_q, w.topk, num_parts, d["tm"].data_ptr(),
+                                     d["so"].data_ptr(), stream))
+        if with_decode:
+            mla.check(L.mla_decode_with_kvcache(ctypes.byref(d["args"]), stream))
+        else:
+            mla.check(L.mla_combine(ctypes.byref(d["args"]), stream))
+
+    stream = torch.cuda.Stream(device=dev)
+    G = n_sets * max(1, 64 // n_sets)  # steps per graph replay
+
+    def capture(n_steps, with_decode=True):
+        g = torch.cuda.CUDAGraph()
+        # warm the path once outside capture
+        with torch.cuda.stream(stream):
+            for k in range(min(n_steps, n_sets)):
+                step(sets[k % n_sets], stream.cuda_stream, with_decode)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(n_steps):
+                step(sets[k % n_sets], torch.cuda.current_stream().cuda_stream, with_decode)
+        torch.cuda.synchronize()
+        return g
+
+    def run_steps(k_steps, full_g, with_decode=True):
+        graphs = []
+        reps, rem = divmod(k_steps, G)
+        for _ in range(reps):
+            graphs.append(full_g)
+        if rem:
+            graphs.append(capture(rem, with_decode))
+        return graphs
+
+    g_full = capture(G)
+    # warmup
+    for gr in run_steps(args.warmup, g_full):
+        gr.replay()
+    torch.cuda.synchronize()
+    timed = run_steps(args.steps, g_full)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for gr in timed:
+        gr.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms_wall = (t1 - t0) * 1e3 / args.steps
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # decode-kernel duration: same steps with the decode launch removed
+    g_nodec = capture(G, with_decode=False)
+    timed_nd = run_steps(args.steps, g_nodec, with_decode=False)
+    for gr in timed_nd[:2]:
+        gr.replay()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for gr in timed_nd:
+        gr.replay()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    rest_ms = f0.elapsed_time(f1) / args.steps
+    decode_ms = max(step_ms - rest_ms, 1e-6)
+
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    kv_gbps_step = kv_bytes / (step_ms * 1e-3) / 1e9
+    kv_gbps_dec = kv_bytes / (decode_ms * 1e-3) / 1e9
+    ai = flops / max(kv_bytes + 2 * q_bytes, 1)
+    hbm_bound = ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(kv_gbps_dec, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(kv_gbps_dec / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        dec_tflops = flops / (decode_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "decode_kernel (split decode)"
+    roof["decode_ms"] = round(decode_ms, 5)
+    roof["per_launch"] = {"flop": flops, "kv_bytes": kv_bytes}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
+            "kv_format": w.kv_format, "causal": w.causal, "topk": w.topk,
+            "sum_seqlens": int(w.cache_seqlens.sum()),
+            "num_parts": num_parts, "rotating_input_sets": n_sets, "graph_steps": G,
+        },
+        "kv_read_GBps": round(kv_gbps_step, 1),
+        "kv_read_frac_hbm": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
+        "tflops_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "ms_per_step_wall": round(step_ms_wall, 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

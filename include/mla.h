@@ -1,0 +1,169 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA decode library, libmla_mi355x.so.
+ *
+ * Computes DeepSeek-style Multi-head Latent Attention decode over a paged
+ * latent KV cache. Pages cited below (by title, then section):
+ *   [Walkthrough] "矩阵、注意力与 GPU：拆解 DeepGEMM 与 FlashMLA" (msy.plus)
+ *   [Guide]       "FlashMLA 实战：MLA 注意力加速指南" (m.lsln.cn)
+ *   [ETAP]        the FlashMLA-ETAP article (ocdem.com)
+ *
+ * The operation ([Walkthrough] §六 "吸收", "结果：decode 变成 MQA"; §五
+ * "公式"): after weight absorption every query head h scores each cached
+ * token against the same 576-dim row [latent c (512) ; rope k^R (64)],
+ * score = softmax_scale * <q[b,i,h,:], row>, and the output is the softmax-
+ * weighted sum of the 512-dim latents. Outputs o[b,i,h,:512] (bf16) and
+ * lse[b,i,h] = ln(sum_t exp(score_t)) (fp32, natural log).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers owned by the caller;
+ *     the library never frees, retains or allocates device memory and never
+ *     synchronises the stream. "host" pointers are read before return.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it; launches are graph-capturable.
+ *   - Return value: MLA_OK (0) or a negative status. On a negative status
+ *     mla_last_error() (thread-local) describes it. Every argument check runs
+ *     on the host before any HIP call, so an invalid call enqueues nothing.
+ *   - Tensors are contiguous, row-major, in the shapes given.
+ */
+#ifndef MLA_MI355X_H
+#define MLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID (-1)     /* bad argument (null pointer, size, flag combination) */
+#define MLA_ERR_UNSUPPORTED (-2) /* well-formed but outside what the kernels handle */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace or metadata buffers too small */
+#define MLA_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+/* KV cache row formats ([Guide] §"FP8 缓存怎么把 KV 压掉四成", §"容易踩的坑"). */
+#define MLA_KV_BF16 0    /* 576 bf16 = 1152 B per token: latent 512, then rope 64 */
+#define MLA_KV_FP8_656 1 /* 656 B per token: 512 e4m3 latent codes, 4 fp32 scales
+                            (one per 128 latent dims), 64 bf16 rope values */
+
+#define MLA_BLOCK_SIZE 64 /* tokens per KV page */
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_MAX_UNITS 8192 /* max row-group sequences (see below) per call */
+
+/*
+ * Split policy (the library's own rule; the pages give the metadata's role,
+ * [Walkthrough] §七 "split-KV", but no format):
+ *   Query rows are grouped into "row groups" of RG heads of one query
+ *   position: RG = 16 when h_q <= 64, else RG = 128. A row-group sequence
+ *   q = b * n_rg + i * n_hb + hb, with n_hb = ceil(h_q / RG) head blocks and
+ *   n_rg = s_q * n_hb, covers T_q = ceil(L_b / 64) tiles of 64 tokens (dense)
+ *   or ceil(topk / 64) tiles (sparse). Units are laid end to end, each
+ *   non-empty one first taking FIXED_COST positions, then one per tile; with
+ *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
+ *   MIN_PAYLOAD), the tile at position x goes to part floor(x / W).
+ *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 2; RG 16 -> 1 and 1.
+ */
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Number of compute units of HIP device `device`, the default num_parts. */
+int mla_default_num_parts(int device, int* num_parts);
+
+/*
+ * Element counts of the two metadata buffers for a call shape:
+ * tile_meta holds num_parts * 8 int32, split_offsets holds Q + 1 int32 where
+ * Q = batch * n_rg. Pure host arithmetic.
+ */
+int mla_metadata_size(int batch, int s_q, int h_q, int num_parts,
+                      int64_t* tile_meta_elems, int64_t* split_offsets_elems);
+
+/*
+ * Bytes of fp32 split workspace mla_decode_with_kvcache needs. Layout, with
+ * S = Q + num_parts slots: partial outputs fp32 [S][RG][512] (each already
+ * divided by its own softmax sum), then, at the next 256-byte boundary,
+ * partial lse fp32 [S][RG]. The slots of row-group sequence q are
+ * split_offsets[q] .. split_offsets[q + 1] - 1, in KV order.
+ */
+int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes);
+
+/*
+ * Split-KV work schedule ([Walkthrough] §七 "split-KV：把长序列切开":
+ * computed once per decode step, reused by every layer).
+ *   cache_seqlens  device int32 [batch]; ignored when topk > 0 (may be NULL)
+ *   topk           0 for dense attention, else the sparse index count
+ *   num_parts      parts (workgroups) of the decode grid, 1..65535
+ *   tile_meta      device int32 [num_parts][8], written: per part
+ *                  {q_begin, t_begin, q_end, t_end (inclusive), first_split,
+ *                   empty, 0, 0}
+ *   split_offsets  device int32 [Q + 1], written: prefix sums of the number
+ *                  of splits of each row-group sequence
+ * The result is a pure function of (cache_seqlens, batch, s_q, h_q, topk,
+ * num_parts). Reusing it after any of these change gives wrong splits
+ * silently; the caller must recompute it ([Walkthrough] §七 warns the same).
+ * Errors: MLA_ERR_INVALID for null buffers, batch/s_q/h_q < 1, topk < 0,
+ * num_parts out of range; MLA_ERR_UNSUPPORTED if Q > MLA_MAX_UNITS.
+ */
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int topk,
+                     int num_parts, int32_t* tile_meta, int32_t* split_offsets, void* stream);
+
+typedef struct mla_decode_args {
+    int32_t struct_size;       /* must equal sizeof(mla_decode_args) */
+    int32_t batch, s_q, h_q;   /* num_heads_k is 1 ([Walkthrough] §六) */
+    const void* q;             /* device bf16 [batch, s_q, h_q, 576]: absorbed latent
+                                  query (512) then rope query (64) */
+    const void* kv;            /* device uint8 [num_blocks, 64, row_bytes] */
+    int64_t num_blocks;        /* pages in the cache; num_blocks*64 < 2^31 */
+    int32_t block_size;        /* must be 64 */
+    int32_t row_bytes;         /* 1152 for MLA_KV_BF16, 656 for MLA_KV_FP8_656; a
+                                  mismatch is rejected ([Guide] §"容易踩的坑") */
+    int32_t kv_format;         /* MLA_KV_BF16 or MLA_KV_FP8_656 */
+    const int32_t* block_table;   /* dense: device int32 [batch, max_blocks_per_seq];
+                                     token t of sequence b is row
+                                     block_table[b, t/64]*64 + t%64 */
+    int32_t max_blocks_per_seq;
+    const int32_t* cache_seqlens; /* dense: device int32 [batch], tokens per sequence */
+    const int32_t* indices;       /* sparse: device int32 [batch, s_q, topk] absolute
+                                     cache rows (page*64 + offset), -1 = unused
+                                     ([Walkthrough] §八 "当前 master 已经是稀疏注意力");
+                                     NULL selects dense attention */
+    int32_t topk;
+    float softmax_scale;
+    int32_t causal;            /* dense only: query i sees t <= L - s_q + i.
+                                  causal with indices -> MLA_ERR_INVALID
+                                  ([Guide] §"容易踩的坑") */
+    const int32_t* tile_meta;     /* from mla_get_metadata with the same shapes */
+    const int32_t* split_offsets;
+    int32_t num_parts;
+    void* workspace;           /* device, >= mla_workspace_size bytes, 256-B aligned */
+    size_t workspace_bytes;
+    void* o;                   /* device bf16 [batch, s_q, h_q, 512], written */
+    float* lse;                /* device fp32 [batch, s_q, h_q], written */
+} mla_decode_args;
+
+/*
+ * Decode attention over the cache.
+ * Enqueues the split kernel, then mla_combine's kernel. Masked tokens (past
+ * L, causal-excluded, -1 or out-of-range sparse entries, tokens whose page id
+ * is outside [0, num_blocks) or past max_blocks_per_seq) are never read and
+ * never contribute. A query row with no attended token gets o = 0 and
+ * lse = -inf. Errors: MLA_ERR_INVALID (see field notes), MLA_ERR_WORKSPACE,
+ * MLA_ERR_UNSUPPORTED, MLA_ERR_HIP.
+ */
+int mla_decode_with_kvcache(const mla_decode_args* args, void* stream);
+
+/*
+ * Split-KV LSE merge ([Walkthrough] §七: m = max m_k,
+ * l = sum l_k e^{m_k - m}, o = sum o_k l_k e^{m_k - m} / l). For every query
+ * row whose sequence has more than one split, merges the partials in the
+ * workspace into o and lse; rows with no split get o = 0, lse = -inf; rows
+ * with one split are left as the split kernel wrote them. Reads the same
+ * fields as mla_decode_with_kvcache (q, kv, block_table, indices unused).
+ */
+int mla_combine(const mla_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_MI355X_H */

@@ -1,0 +1,201 @@
+// C ABI of the library (declared in include/mla.h): argument validation on
+// the host, buffer sizing, and kernel launches. Every check runs before any
+// HIP call so that an invalid call enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int check_shape(int batch, int s_q, int h_q, int num_parts) {
+    if (batch < 1) return fail(MLA_ERR_INVALID, "batch must be >= 1 (got %d)", batch);
+    if (s_q < 1) return fail(MLA_ERR_INVALID, "s_q must be >= 1 (got %d)", s_q);
+    if (h_q < 1) return fail(MLA_ERR_INVALID, "h_q must be >= 1 (got %d)", h_q);
+    if (num_parts < 1 || num_parts > 65535)
+        return fail(MLA_ERR_INVALID, "num_parts must be in [1, 65535] (got %d)", num_parts);
+    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const int64_t Q = (int64_t)batch * l.n_rg;
+    if (Q > mla::kMaxUnits)
+        return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * ceil(h_q / %d) = %lld exceeds %d row-group sequences",
+                    l.rg, (long long)Q, mla::kMaxUnits);
+    return MLA_OK;
+}
+
+size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
+    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const size_t slots = (size_t)batch * l.n_rg + (size_t)num_parts;
+    const size_t o_bytes = slots * l.rg * mla::kDv * sizeof(float);
+    const size_t lse_bytes = slots * l.rg * sizeof(float);
+    return ((o_bytes + 255) & ~(size_t)255) + lse_bytes;
+}
+
+// Validates a decode call; fills the kernel parameters.
+int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
+    if (!a) return fail(MLA_ERR_INVALID, "args is NULL");
+    if (a->struct_size != (int32_t)sizeof(mla_decode_args))
+        return fail(MLA_ERR_INVALID, "struct_size %d != sizeof(mla_decode_args) %d", a->struct_size,
+                    (int)sizeof(mla_decode_args));
+    int st = check_shape(a->batch, a->s_q, a->h_q, a->num_parts);
+    if (st) return st;
+    if (!a->q || !a->kv || !a->o || !a->lse) return fail(MLA_ERR_INVALID, "q, kv, o and lse must be non-NULL");
+    if (!aligned(a->q, 16) || !aligned(a->o, 16) || !aligned(a->kv, 16) || !aligned(a->lse, 4))
+        return fail(MLA_ERR_INVALID, "q, o and kv must be 16-byte aligned, lse 4-byte aligned");
+    if (a->block_size != mla::kBlock) return fail(MLA_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
+    if (a->kv_format != MLA_KV_BF16 && a->kv_format != MLA_KV_FP8_656)
+        return fail(MLA_ERR_INVALID, "unknown kv_format %d", a->kv_format);
+    const int want_row = a->kv_format == MLA_KV_BF16 ? 1152 : 656;
+    if (a->row_bytes != want_row)
+        return fail(MLA_ERR_INVALID, "row_bytes %d does not match kv_format %s (%d bytes per token)", a->row_bytes,
+                    a->kv_format == MLA_KV_BF16 ? "bf16" : "fp8-656", want_row);
+    if (a->num_blocks < 1) return fail(MLA_ERR_INVALID, "num_blocks must be >= 1");
+    if (a->num_blocks * (int64_t)mla::kBlock >= ((int64_t)1 << 31))
+        return fail(MLA_ERR_UNSUPPORTED, "num_blocks * 64 must be < 2^31");
+    const bool sparse = a->indices != nullptr;
+    if (sparse) {
+        if (a->topk < 1) return fail(MLA_ERR_INVALID, "topk must be >= 1 with indices");
+        if (a->causal) return fail(MLA_ERR_INVALID, "causal masking is not defined with sparse indices");
+    } else {
+        if (!a->block_table || !a->cache_seqlens)
+            return fail(MLA_ERR_INVALID, "dense attention needs block_table and cache_seqlens");
+        if (a->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+        if (a->topk != 0) return fail(MLA_ERR_INVALID, "topk must be 0 without indices");
+    }
+    if (!std::isfinite(a->softmax_scale)) return fail(MLA_ERR_INVALID, "softmax_scale must be finite");
+    if (!a->tile_meta || !a->split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
+    if (!a->workspace) return fail(MLA_ERR_INVALID, "workspace is required");
+    if (!aligned(a->workspace, 256)) return fail(MLA_ERR_INVALID, "workspace must be 256-byte aligned");
+    const size_t need = workspace_bytes(a->batch, a->s_q, a->h_q, a->num_parts);
+    if (a->workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", a->workspace_bytes, need);
+
+    const mla::Layout l = mla::layout_for(a->h_q, a->s_q);
+    const size_t slots = (size_t)a->batch * l.n_rg + (size_t)a->num_parts;
+    const size_t o_bytes = ((slots * l.rg * mla::kDv * sizeof(float)) + 255) & ~(size_t)255;
+    p->q = static_cast<const uint16_t*>(a->q);
+    p->kv = static_cast<const uint8_t*>(a->kv);
+    p->block_table = a->block_table;
+    p->seqlens = a->cache_seqlens;
+    p->indices = a->indices;
+    p->tile_meta = a->tile_meta;
+    p->split_offsets = a->split_offsets;
+    p->ws_o = static_cast<float*>(a->workspace);
+    p->ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + o_bytes);
+    p->o = static_cast<uint16_t*>(a->o);
+    p->lse = a->lse;
+    p->batch = a->batch;
+    p->s_q = a->s_q;
+    p->h_q = a->h_q;
+    p->n_hb = l.n_hb;
+    p->n_rg = l.n_rg;
+    p->rg = l.rg;
+    p->mbps = sparse ? 0 : a->max_blocks_per_seq;
+    p->topk = sparse ? a->topk : 0;
+    p->causal = a->causal ? 1 : 0;
+    p->num_rows = (int)(a->num_blocks * mla::kBlock);
+    p->num_parts = a->num_parts;
+    p->row_bytes = a->row_bytes;
+    p->scale_log2 = a->softmax_scale * 1.4426950408889634f;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_err; }
+
+int mla_default_num_parts(int device, int* num_parts) {
+    if (!num_parts) return fail(MLA_ERR_INVALID, "num_parts is NULL");
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    *num_parts = n;
+    return ok();
+}
+
+int mla_metadata_size(int batch, int s_q, int h_q, int num_parts, int64_t* tile_meta_elems,
+                      int64_t* split_offsets_elems) {
+    if (!tile_meta_elems || !split_offsets_elems) return fail(MLA_ERR_INVALID, "output pointers are NULL");
+    int st = check_shape(batch, s_q, h_q, num_parts);
+    if (st) return st;
+    const mla::Layout l = mla::layout_for(h_q, s_q);
+    *tile_meta_elems = (int64_t)num_parts * 8;
+    *split_offsets_elems = (int64_t)batch * l.n_rg + 1;
+    return ok();
+}
+
+int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes) {
+    if (!bytes) return fail(MLA_ERR_INVALID, "bytes is NULL");
+    int st = check_shape(batch, s_q, h_q, num_parts);
+    if (st) return st;
+    *bytes = workspace_bytes(batch, s_q, h_q, num_parts);
+    return ok();
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int topk, int num_parts,
+                     int32_t* tile_meta, int32_t* split_offsets, void* stream) {
+    int st = check_shape(batch, s_q, h_q, num_parts);
+    if (st) return st;
+    if (topk < 0) return fail(MLA_ERR_INVALID, "topk must be >= 0 (got %d)", topk);
+    if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
+    if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
+    const mla::Layout l = mla::layout_for(h_q, s_q);
+    mla::MetaParams p;
+    p.seqlens = cache_seqlens;
+    p.tile_meta = tile_meta;
+    p.split_offsets = split_offsets;
+    p.batch = batch;
+    p.n_rg = l.n_rg;
+    p.topk = topk;
+    p.num_parts = num_parts;
+    p.fixed_cost = l.fixed_cost;
+    p.min_payload = l.min_payload;
+    hipError_t e = mla::launch_metadata(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_decode_with_kvcache(const mla_decode_args* args, void* stream) {
+    mla::DecodeParams p;
+    int st = prepare(args, &p);
+    if (st) return st;
+    const mla::Layout l = mla::layout_for(args->h_q, args->s_q);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format == MLA_KV_FP8_656, args->indices != nullptr, s);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    e = mla::launch_combine(p, s);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_combine(const mla_decode_args* args, void* stream) {
+    mla::DecodeParams p;
+    int st = prepare(args, &p);
+    if (st) return st;
+    hipError_t e = mla::launch_combine(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

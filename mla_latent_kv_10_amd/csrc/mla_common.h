@@ -1,0 +1,74 @@
+// Shared device/host definitions of the gfx950 MLA decode library.
+//
+// Pages cited (by title, then section):
+//   [Walkthrough] "矩阵、注意力与 GPU：拆解 DeepGEMM 与 FlashMLA" (msy.plus)
+//   [Guide]       "FlashMLA 实战：MLA 注意力加速指南" (m.lsln.cn)
+//   [ETAP]        the FlashMLA-ETAP article (ocdem.com)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kBlock = 64;          // tokens per KV page and per tile
+constexpr int kDqk = 576;           // 512 latent + 64 rope ([Walkthrough] §六)
+constexpr int kDv = 512;            // value = latent
+constexpr int kUnits = 72;          // 16-byte units per bf16 row (1152 B)
+constexpr int kTileBytes = kBlock * 1152;       // one bf16 tile in LDS (swizzled)
+constexpr int kRawRow = 656;        // FP8 row ([Guide] §"FP8 缓存怎么把 KV 压掉四成")
+constexpr int kRawUnits = 41;       // 656 / 16
+constexpr int kRawTileBytes = kBlock * kRawRow; // one FP8 tile as stored, 41 x 1 KB
+constexpr int kMaxUnits = 8192;     // row-group sequences per call (metadata LDS)
+constexpr int kThreads = 256;       // four wave64s per workgroup
+
+enum Variant { kV128 = 0, kV16 = 1 };
+
+// Row-group policy; it is part of the ABI contract (see include/mla.h).
+struct Layout {
+    int rg;           // heads per row group
+    int n_hb;         // head blocks
+    int n_rg;         // row groups per batch entry (s_q * n_hb)
+    int fixed_cost;   // schedule positions charged per row-group sequence
+    int min_payload;  // minimum schedule positions per part
+    int variant;
+};
+
+inline Layout layout_for(int h_q, int s_q) {
+    Layout l;
+    if (h_q <= 64) { l.rg = 16; l.fixed_cost = 1; l.min_payload = 1; l.variant = kV16; }
+    else           { l.rg = 128; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV128; }
+    l.n_hb = (h_q + l.rg - 1) / l.rg;
+    l.n_rg = s_q * l.n_hb;
+    return l;
+}
+
+struct MetaParams {
+    const int32_t* seqlens;
+    int32_t* tile_meta;
+    int32_t* split_offsets;
+    int batch, n_rg, topk, num_parts, fixed_cost, min_payload;
+};
+
+struct DecodeParams {
+    const uint16_t* q;          // bf16 bits [B, s_q, h_q, 576]
+    const uint8_t* kv;          // [num_rows, row_bytes]
+    const int32_t* block_table; // [B, mbps]
+    const int32_t* seqlens;     // [B]
+    const int32_t* indices;     // [B, s_q, topk]
+    const int32_t* tile_meta;   // [num_parts, 8]
+    const int32_t* split_offsets;
+    float* ws_o;                // [slots, rg, 512]
+    float* ws_lse;              // [slots, rg]
+    uint16_t* o;                // bf16 bits [B, s_q, h_q, 512]
+    float* lse;                 // [B, s_q, h_q]
+    int batch, s_q, h_q, n_hb, n_rg, rg, mbps, topk, causal, num_rows, num_parts, row_bytes;
+    float scale_log2;           // softmax_scale * log2(e)
+};
+
+// Host-side launchers (defined in the .hip files).
+hipError_t launch_metadata(const MetaParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int variant, bool fp8, bool sparse, hipStream_t s);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t s);
+
+}  // namespace mla

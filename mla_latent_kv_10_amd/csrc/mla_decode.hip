@@ -1,0 +1,644 @@
+// MLA decode split kernel for gfx950 (CDNA4), plus its launcher.
+//
+// What it computes ([Walkthrough] §六 "结果：decode 变成 MQA", §五 "公式";
+// §七 "split-KV"): for each row group (RG query heads of one query position
+// of one sequence) and a contiguous range of 64-token tiles, the online-
+// softmax attention state (running max m, running sum l, unnormalised output
+// O) over those tokens; then either the final o = O / l and lse, or the
+// normalised partial (O / l, lse) for the split merge.
+//
+// gfx950 design (differs from the pages' Hopper designs):
+//  * Tiles go HBM -> LDS with buffer_load ... lds (no VGPR staging), through a
+//    structured buffer descriptor (stride = row bytes, records = cache rows):
+//    each lane names its token's row; a masked token gets an out-of-range
+//    index and the hardware writes zeros, so masked rows are never read.
+//    Two tiles are in flight (double buffering); waits are explicit vmcnt
+//    counts plus raw s_barrier, so prefetches stay outstanding.
+//  * The bf16 tile sits in LDS as 72 chunks of 1 KB (8 tokens x 8 16-byte
+//    units), with the unit index XOR-swizzled by (token/2) so that 16 lanes
+//    reading 16 tokens at one unit hit 16 distinct bank groups.
+//  * Scores are computed transposed, S^T = K . Q^T, with tokens on the MFMA
+//    M dimension ([ETAP] §2.1-2.3 puts the long KV axis on M): each lane then
+//    owns one query row, so the softmax max/sum are in-lane plus one cross-
+//    half (or cross-quarter) shuffle, and P^T feeds the PV MFMA straight from
+//    registers. The V operand is the transposed view of the same LDS tile,
+//    read with ds_read_b64_tr_b16.
+//  * FP8 rows (656 B) land raw in LDS, then every thread dequantises
+//    bf16_rne(fp32(e4m3) * fp32 scale) into the bf16 tile once for all waves
+//    ([Guide] §"Crossover" explains the dequant cost; on CDNA4 one workgroup
+//    dequantises a tile once instead of exchanging halves between CTAs).
+//  * The running max is updated lazily: the exponent reference moves only
+//    when a row's max grows by more than 2^8 (exact in real arithmetic; keeps
+//    the O rescale off the common path).
+#include <type_traits>
+
+#include "mla_common.h"
+
+namespace mla {
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;  // exponent reference moves when a row max grows by > 2^8
+constexpr unsigned kOOB = 0xFFFFFFFFu;
+
+// ---------------------------------------------------------------- LDS layout
+
+// Byte offset of (token t, 16-byte unit u) inside a swizzled bf16 tile.
+__device__ __forceinline__ int tile_off(int t, int u) {
+    return (((t >> 3) * 9 + (u >> 3)) << 10) + ((((t & 7) << 3) | ((u & 7) ^ ((t >> 1) & 7))) << 4);
+}
+
+template <bool FP8>
+struct Smem {
+    // bf16: two tiles (double buffer). FP8: two raw tiles + one bf16 tile.
+    static constexpr int kTileA = 0;
+    static constexpr int kTileB = FP8 ? -1 : kTileBytes;
+    static constexpr int kRaw0 = FP8 ? kTileBytes : -1;
+    static constexpr int kRaw1 = FP8 ? kTileBytes + kRawTileBytes : -1;
+    static constexpr int kBytes = FP8 ? kTileBytes + 2 * kRawTileBytes : 2 * kTileBytes;
+};
+
+// ---------------------------------------------------------------- waits
+
+__device__ __forceinline__ void wait_vm(int n) {
+    // vmcnt takes an immediate; n is wave-uniform and small.
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+        case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
+        case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+__device__ __forceinline__ void block_sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane direct load into LDS: lane i's bytes land at dst + 16 i.
+// Global address = base + vindex * stride + voffset + soffset; an out-of-range
+// vindex writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char LDS_AS* dst, unsigned vindex, unsigned voffset,
+                                      int soffset) {
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, vindex, voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// bf16x8 from eight floats (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const char LDS_AS* p) { return *(const bf16x8 LDS_AS*)p; }
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char LDS_AS* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p);
+}
+
+
+// acc *= alpha for an accumulator held in AGPRs. Written as inline asm on the
+// AGPRs themselves so the register allocator keeps MFMA accumulators in the
+// AGPR file (a VALU multiply in C++ would make it migrate them to VGPRs). The
+// trailing s_nop covers the VALU-write -> MFMA-srcC hazard; the last MFMA
+// that wrote acc is hundreds of cycles back (a whole QK phase).
+template <typename V, int N>
+__device__ __forceinline__ void scale_agpr(V& acc, float alpha) {
+    #pragma unroll
+    for (int e = 0; e < N; ++e) {
+        float x = acc[e], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t) : "v"(alpha));
+        acc[e] = x;
+    }
+}
+
+// ---------------------------------------------------------------- segment context
+
+struct Seg {
+    int b, i, h0, limit, t_end, split, n_splits, slot, mask_rows;
+};
+
+// Row index of token t of tile k (dense): page base from the block table.
+// Returns kOOB for masked tokens.
+__device__ __forceinline__ unsigned dense_row(int page_row0, int n_valid, int t) {
+    return (page_row0 >= 0 && t < n_valid) ? (unsigned)(page_row0 + t) : kOOB;
+}
+
+// ---------------------------------------------------------------- kernel
+
+template <bool FP8, bool SPARSE, int VAR>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
+    using S = Smem<FP8>;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S::kBytes];
+    char LDS_AS* smem = (char LDS_AS*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+
+    // XCD-aware part numbering: hardware places workgroup x on XCD x % 8, so
+    // consecutive logical parts (same sequence) share an XCD and its L2.
+    int part = blockIdx.x;
+    if ((gridDim.x & 7) == 0) part = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int32_t* tm = p.tile_meta + (int64_t)part * 8;
+    if (uniform(tm[5])) return;
+    const int qb = uniform(tm[0]), tb = uniform(tm[1]), qe = uniform(tm[2]), te = uniform(tm[3]);
+    const int fs = uniform(tm[4]);
+
+    const __amdgpu_buffer_rsrc_t kv_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)p.row_bytes, p.num_rows, 0x00020000);
+
+    constexpr int RG = (VAR == kV128) ? 128 : 16;
+
+    for (int qq = qb; qq <= qe; ++qq) {
+        Seg sg;
+        sg.b = qq / p.n_rg;
+        const int rgi = qq - sg.b * p.n_rg;
+        sg.i = rgi / p.n_hb;
+        sg.h0 = (rgi - sg.i * p.n_hb) * RG;
+        int T_q;
+        if (SPARSE) {
+            T_q = (p.topk + kBlock - 1) / kBlock;
+            sg.limit = p.topk;
+        } else {
+            const int L = uniform(p.seqlens[sg.b]);
+            T_q = L > 0 ? (L + kBlock - 1) / kBlock : 0;
+            int lim = p.causal ? L - p.s_q + 1 + sg.i : L;
+            lim = min(lim, min(L, p.mbps * kBlock));
+            sg.limit = max(lim, 0);
+        }
+        const int t0 = (qq == qb) ? tb : 0;
+        int t1 = (qq == qe) ? te : T_q - 1;
+        sg.split = (qq == qb) ? fs : 0;
+        const int so = uniform(p.split_offsets[qq]);
+        sg.n_splits = uniform(p.split_offsets[qq + 1]) - so;
+        sg.slot = so + sg.split;
+        const int t_eff = (sg.limit + kBlock - 1) / kBlock;  // tiles holding any attended token
+        t1 = min(t1, t_eff - 1);
+        sg.t_end = t1;
+
+        // ------------------------------------------------ per-segment state
+        const int64_t qrow0 = ((int64_t)sg.b * p.s_q + sg.i) * p.h_q;  // row index of head 0
+        const int32_t* idx_row = SPARSE ? p.indices + ((int64_t)sg.b * p.s_q + sg.i) * p.topk : nullptr;
+
+        // Sparse: lane l holds the row of token l of a tile (kOOB when masked).
+        auto sparse_row = [&](int k) -> unsigned {
+            const int pos = k * kBlock + lane;
+            unsigned r = kOOB;
+            if (k <= t1 && pos < p.topk) {
+                const int v = idx_row[pos];
+                r = (v >= 0 && v < p.num_rows) ? (unsigned)v : kOOB;
+            }
+            return r;
+        };
+        // Dense: row of token 0 of tile k, or -1 when the page id is invalid.
+        // Read through the constant address space so the uniform load is a
+        // scalar one (it does not count against vmcnt).
+        const int32_t __attribute__((address_space(4)))* bt_c =
+            (const int32_t __attribute__((address_space(4)))*)p.block_table;
+        auto dense_page_row0 = [&](int k) -> int {
+            const int blk = uniform(bt_c[(int64_t)sg.b * p.mbps + k]);
+            return (blk >= 0 && (int64_t)blk * kBlock < (int64_t)p.num_rows) ? blk * kBlock : -1;
+        };
+
+        // Issue the DMA of tile k into LDS region `dst`; returns the tile's
+        // validity mask (bit t set = token t attended). The number of VMEM
+        // instructions per wave is fixed per variant (n_dma).
+        auto issue_tile = [&](int k, char LDS_AS* dst, unsigned srow) -> uint64_t {
+            int page0 = 0, n_valid = 0;
+            uint64_t mask;
+            if (!SPARSE) {
+                page0 = dense_page_row0(k);
+                n_valid = min(kBlock, sg.limit - k * kBlock);
+                mask = (page0 < 0 || n_valid <= 0) ? 0ull : (n_valid >= 64 ? ~0ull : ((1ull << n_valid) - 1ull));
+            } else {
+                mask = __builtin_amdgcn_ballot_w64(srow != kOOB);
+            }
+            if (!FP8) {
+                // 72 chunks, 18 per wave: token groups 2w, 2w+1; unit groups 0..8.
+                #pragma unroll 1
+                for (int g = 0; g < 2; ++g) {
+                    const int tg = 2 * wave + g;
+                    const int t = tg * 8 + (lane >> 3);
+                    const int uu = (lane & 7) ^ ((t >> 1) & 7);
+                    unsigned row;
+                    if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
+                    else row = dense_row(page0, n_valid, t);
+                    #pragma unroll 1
+                    for (int ug = 0; ug < 9; ++ug) {
+                        dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                    }
+                }
+            } else {
+                // 41 chunks of the raw tile image, chunk c to wave c % 4.
+                #pragma unroll 1
+                for (int c = wave; c < kRawUnits; c += 4) {
+                    const int kk = c * 64 + lane;
+                    const int t = kk / kRawUnits;
+                    const int u = kk - t * kRawUnits;
+                    unsigned row;
+                    if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
+                    else row = dense_row(page0, n_valid, t);
+                    dma16(kv_rsrc, dst + (c << 10), row, (unsigned)(u << 4), 0);
+                }
+            }
+            return mask;
+        };
+        const int n_dma = FP8 ? (wave == 0 ? 11 : 10) : 18;
+
+        // Dequantise raw FP8 tile `raw` into the bf16 tile at `tile`.
+        auto dequant = [&](const char LDS_AS* raw, char LDS_AS* tile) {
+            // latent: 64 tokens x 32 raw units (16 codes each); lanes walk tokens
+            #pragma unroll 1
+            for (int j = 0; j < 8; ++j) {
+                const int item = tid + j * kThreads;
+                const int t = item & 63, pu = item >> 6;
+                const u32x4 c = *(const u32x4 LDS_AS*)(raw + t * kRawRow + pu * 16);
+                const float sc = *(const float LDS_AS*)(raw + t * kRawRow + 512 + (pu >> 3) * 4);
+                float v[16];
+                #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], false);
+                    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], true);
+                    v[4 * d + 0] = lo[0] * sc; v[4 * d + 1] = lo[1] * sc;
+                    v[4 * d + 2] = hi[0] * sc; v[4 * d + 3] = hi[1] * sc;
+                }
+                *(bf16x8 LDS_AS*)(tile + tile_off(t, 2 * pu)) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                *(bf16x8 LDS_AS*)(tile + tile_off(t, 2 * pu + 1)) = pack8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+            }
+            // rope: 64 tokens x 8 units of bf16, copied
+            #pragma unroll 1
+            for (int j = 0; j < 2; ++j) {
+                const int item = tid + j * kThreads;
+                const int t = item & 63, r = item >> 6;
+                const u32x4 c = *(const u32x4 LDS_AS*)(raw + t * kRawRow + 528 + r * 16);
+                *(u32x4 LDS_AS*)(tile + tile_off(t, 64 + r)) = c;
+            }
+        };
+
+        // ------------------------------------------------ compute state
+        // V128: wave owns rows 32*wave + (lane & 31); all 64 tokens of a tile.
+        // V16 : wave owns tokens 16*wave .. +15 of each tile; all 16 rows.
+        constexpr int NQ = (VAR == kV128) ? 36 : 18;   // k-steps over 576 dims
+        constexpr int NO = (VAR == kV128) ? 16 : 32;   // output blocks over 512 dims
+        bf16x8 qreg[NQ];
+        typedef typename std::conditional<VAR == kV128, f32x16, f32x4>::type Acc;
+        Acc oacc[NO];
+        #pragma unroll
+        for (int d = 0; d < NO; ++d) oacc[d] = Acc{};
+        float m_run = -INFINITY;  // exponent reference (log2 units), per row
+        float l_run = 0.f;        // partial sum of p over this lane's tokens
+
+        {
+            int row, dsub;
+            if constexpr (VAR == kV128) { row = 32 * wave + (lane & 31); dsub = 8 * (lane >> 5); }
+            else { row = lane & 15; dsub = 8 * (lane >> 4); }
+            const int h = sg.h0 + row;
+            const bool ok = h < p.h_q;
+            const uint16_t* qp = p.q + (qrow0 + (ok ? h : 0)) * kDqk + dsub;
+            #pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) {
+                const int dim0 = (VAR == kV128) ? 16 * kk : 32 * kk;
+                i16x8 v = *(const i16x8*)(qp + dim0);
+                if (!ok) v = i16x8{};
+                qreg[kk] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+
+        // Per-lane LDS offsets (see the layout derivation in the comments).
+        int koff[2][4];   // V128: [token block][k-step & 3]; V16 uses koff[0][0..1]
+        int voff[4];      // V128: [lohi*2 + (d&1)]; V16: [d&3]
+        if constexpr (VAR == kV128) {
+            const int hh = lane >> 5;
+            #pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int t = 32 * blk + (lane & 31);
+                const int base = ((t >> 3) * 9 << 10) + ((t & 7) << 7);
+                const int x = (t >> 1) & 7;
+                #pragma unroll
+                for (int j = 0; j < 4; ++j) koff[blk][j] = base + ((((2 * j + hh) ^ x) & 7) << 4);
+            }
+            const int q16 = lane >> 4, r = (lane >> 2) & 3, c4 = lane & 3;
+            #pragma unroll
+            for (int lohi = 0; lohi < 2; ++lohi) {
+                #pragma unroll
+                for (int dp = 0; dp < 2; ++dp) {
+                    const int tt = 4 * hh + r;                          // token & 7
+                    const int x = (4 * lohi + 2 * hh + (r >> 1)) & 7;   // (token >> 1) & 7
+                    const int u7 = 4 * dp + 2 * (q16 & 1) + (c4 >> 1);  // unit & 7
+                    voff[lohi * 2 + dp] = (((tt << 3) | (u7 ^ x)) << 4) + 8 * (c4 & 1);
+                }
+            }
+        } else {
+            const int g = lane >> 4;
+            const int t = 16 * wave + (lane & 15);
+            #pragma unroll
+            for (int j = 0; j < 2; ++j)
+                koff[0][j] = ((t >> 3) * 9 << 10) + ((((t & 7) << 3) | (((4 * j + g) ^ ((t >> 1) & 7)) & 7)) << 4);
+            koff[1][0] = koff[1][1] = koff[1][2] = koff[1][3] = koff[0][2] = koff[0][3] = 0;
+            const int r = (lane >> 2) & 3, c4 = lane & 3;
+            const int tv = 16 * wave + 4 * g + r;
+            #pragma unroll
+            for (int dq = 0; dq < 4; ++dq) {
+                const int u7 = 2 * dq + (c4 >> 1);
+                voff[dq] = ((tv >> 3) * 9 << 10) + ((((tv & 7) << 3) | ((u7 ^ ((tv >> 1) & 7)) & 7)) << 4) + 8 * (c4 & 1);
+            }
+        }
+
+        // ------------------------------------------------ compute one tile
+        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask) {
+            if constexpr (VAR == kV128) {
+                f32x16 s0 = {}, s1 = {};
+                #pragma unroll
+                for (int kk = 0; kk < 36; ++kk) {
+                    const int off = (kk >> 2) << 10;
+                    const bf16x8 a0 = lds_read16(tile + koff[0][kk & 3] + off);
+                    const bf16x8 a1 = lds_read16(tile + koff[1][kk & 3] + off);
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // lane holds row (lane&31), token 32*blk + 8*(v>>2) + 4*(lane>>5) + (v&3)
+                const int hh = lane >> 5;
+                #pragma unroll
+                for (int v = 0; v < 16; ++v) { s0[v] *= p.scale_log2; s1[v] *= p.scale_log2; }
+                if (mask != ~0ull) {
+                    const uint64_t mh = mask >> (4 * hh);
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int t = 8 * (v >> 2) + (v & 3);
+                        if (!((mh >> t) & 1ull)) s0[v] = -INFINITY;
+                        if (!((mh >> (32 + t)) & 1ull)) s1[v] = -INFINITY;
+                    }
+                }
+                float mt = fmaxf(s0[0], s1[0]);
+                #pragma unroll
+                for (int v = 1; v < 16; ++v) mt = fmaxf(mt, fmaxf(s0[v], s1[v]));
+                mt = fmaxf(mt, wave_shfl_xor(mt, 32));
+                const bool need = mt > m_run + kLazyMax;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+                    #pragma unroll
+                    for (int d = 0; d < 16; ++d) scale_agpr<f32x16, 16>(oacc[d], alpha);
+                    asm volatile("s_nop 2" ::: "memory");
+                    m_run = m_new;
+                }
+                const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+                float ps = 0.f;
+                #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    s0[v] = __builtin_amdgcn_exp2f(s0[v] - mu);
+                    s1[v] = __builtin_amdgcn_exp2f(s1[v] - mu);
+                    ps += s0[v] + s1[v];
+                }
+                l_run += ps;
+                bf16x8 pb[4];
+                #pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    pb[c] = pack8(s0[8 * c + 0], s0[8 * c + 1], s0[8 * c + 2], s0[8 * c + 3],
+                                  s0[8 * c + 4], s0[8 * c + 5], s0[8 * c + 6], s0[8 * c + 7]);
+                    pb[2 + c] = pack8(s1[8 * c + 0], s1[8 * c + 1], s1[8 * c + 2], s1[8 * c + 3],
+                                      s1[8 * c + 4], s1[8 * c + 5], s1[8 * c + 6], s1[8 * c + 7]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                #pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    #pragma unroll
+                    for (int d = 0; d < 16; ++d) {
+                        const int off_lo = ((2 * c) * 9 + (d >> 1)) << 10;
+                        const int off_hi = ((2 * c + 1) * 9 + (d >> 1)) << 10;
+                        const i16x4 lo = lds_read_tr(tile + voff[0 * 2 + (d & 1)] + off_lo);
+                        const i16x4 hi = lds_read_tr(tile + voff[1 * 2 + (d & 1)] + off_hi);
+                        const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[c], oacc[d], 0, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                f32x4 s = {};
+                #pragma unroll
+                for (int kk = 0; kk < 18; ++kk) {
+                    const bf16x8 a = lds_read16(tile + koff[0][kk & 1] + ((kk >> 1) << 10));
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s, 0, 0, 0);
+                }
+                // lane holds row (lane&15), tokens 16*wave + 4*(lane>>4) + v
+                const int g = lane >> 4;
+                float x[4];
+                #pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    x[v] = s[v] * p.scale_log2;
+                    const int t = 16 * wave + 4 * g + v;
+                    if (!((mask >> t) & 1ull)) x[v] = -INFINITY;
+                }
+                float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                mt = fmaxf(mt, wave_shfl_xor(mt, 16));
+                mt = fmaxf(mt, wave_shfl_xor(mt, 32));
+                const bool need = mt > m_run + kLazyMax;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+                    #pragma unroll
+                    for (int d = 0; d < 32; ++d) scale_agpr<f32x4, 4>(oacc[d], alpha);
+                    asm volatile("s_nop 2" ::: "memory");
+                    m_run = m_new;
+                }
+                const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+                #pragma unroll
+                for (int v = 0; v < 4; ++v) { x[v] = __builtin_amdgcn_exp2f(x[v] - mu); l_run += x[v]; }
+                const bf16x8 pb = pack8(x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f);
+                #pragma unroll
+                for (int d = 0; d < 32; ++d) {
+                    const i16x4 lo = lds_read_tr(tile + voff[d & 3] + ((d >> 2) << 10));
+                    const i16x8 av = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+                    oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[d], 0, 0, 0);
+                }
+            }
+        };
+
+        // ------------------------------------------------ tile pipeline
+        if (t0 <= t1) {
+            char LDS_AS* stage0 = smem + (FP8 ? S::kRaw0 : S::kTileA);
+            char LDS_AS* stage1 = smem + (FP8 ? S::kRaw1 : S::kTileB);
+            char LDS_AS* ctile = smem + S::kTileA;  // FP8: the single bf16 tile
+            unsigned idx_a = kOOB, idx_b = kOOB, idx_c = kOOB;  // sparse rows of tiles k, k+1, k+2
+            if (SPARSE) {
+                idx_a = sparse_row(t0);
+                idx_b = sparse_row(t0 + 1);
+                idx_c = sparse_row(t0 + 2);
+            }
+            uint64_t mask_a = issue_tile(t0, stage0, idx_a), mask_b = 0;
+            if (t0 + 1 <= t1) mask_b = issue_tile(t0 + 1, stage1, idx_b);
+            for (int k = t0; k <= t1; ++k) {
+                const bool odd = ((k - t0) & 1) != 0;
+                char LDS_AS* cur = odd ? stage1 : stage0;
+                unsigned idx_d = kOOB;
+                if (SPARSE && k + 3 <= t1) idx_d = sparse_row(k + 3);
+                // VMEM instructions this wave issued after tile k's DMA (a
+                // lower bound is safe: it only waits longer).
+                int after = 0;
+                if (k + 1 <= t1) {
+                    after += n_dma;
+                    if (SPARSE) {
+                        if (k > t0 && k + 2 <= t1) after += 1;
+                        if (k + 3 <= t1) after += 1;
+                    }
+                }
+                wait_vm(after);
+                block_sync_lds();
+                uint64_t mask_c = 0;
+                if (FP8) {
+                    dequant(cur, ctile);
+                    block_sync_lds();
+                    if (k + 2 <= t1) mask_c = issue_tile(k + 2, cur, idx_c);
+                    compute_tile(ctile, mask_a);
+                } else {
+                    compute_tile(cur, mask_a);
+                    block_sync_lds();
+                    if (k + 2 <= t1) mask_c = issue_tile(k + 2, cur, idx_c);
+                }
+                idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
+                mask_a = mask_b; mask_b = mask_c;
+            }
+            block_sync_lds();  // every wave is done with the tiles before LDS is reused
+        }
+
+        // ------------------------------------------------ epilogue
+        const bool final_out = sg.n_splits == 1;
+        if constexpr (VAR == kV128) {
+            const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            const int rloc = 32 * wave + (lane & 31);
+            const int h = sg.h0 + rloc;
+            const int hh = lane >> 5;
+            if (final_out) {
+                if (h < p.h_q) {
+                    uint16_t* op = p.o + (qrow0 + h) * kDv;
+                    #pragma unroll
+                    for (int d = 0; d < 16; ++d) {
+                        #pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int dim = 32 * d + 8 * g + 4 * hh;
+                            i16x4 w;
+                            #pragma unroll
+                            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, (__bf16)(oacc[d][4 * g + e] * inv));
+                            *(i16x4*)(op + dim) = w;
+                        }
+                    }
+                    if (hh == 0) p.lse[qrow0 + h] = lse_v;
+                }
+            } else {
+                float* wp = p.ws_o + ((int64_t)sg.slot * RG + rloc) * kDv;
+                #pragma unroll
+                for (int d = 0; d < 16; ++d) {
+                    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int dim = 32 * d + 8 * g + 4 * hh;
+                        f32x4 w = {oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv, oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv};
+                        *(f32x4*)(wp + dim) = w;
+                    }
+                }
+                if (hh == 0) p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
+            }
+        } else {
+            // merge the four waves' states through LDS
+            float l_w = l_run + wave_shfl_xor(l_run, 16);
+            l_w += wave_shfl_xor(l_w, 32);
+            float LDS_AS* mo = (float LDS_AS*)smem;                  // [4][16][512]
+            float LDS_AS* mm = (float LDS_AS*)(smem + 4 * 16 * 512 * 4);  // [4][16] m, then [4][16] l
+            const int row = lane & 15, g = lane >> 4;
+            #pragma unroll
+            for (int d = 0; d < 32; ++d)
+                *(f32x4 LDS_AS*)(mo + (wave * 16 + row) * 512 + 16 * d + 4 * g) = oacc[d];
+            if (g == 0) { mm[wave * 16 + row] = m_run; mm[64 + wave * 16 + row] = l_w; }
+            block_sync_lds();
+            const int mr = tid >> 4;           // row 0..15
+            const int dseg = (tid & 15) * 32;  // 32 dims per thread
+            float mw[4], lw[4];
+            float mx = -INFINITY;
+            #pragma unroll
+            for (int w = 0; w < 4; ++w) { mw[w] = mm[w * 16 + mr]; lw[w] = mm[64 + w * 16 + mr]; mx = fmaxf(mx, mw[w]); }
+            float e[4], l_tot = 0.f;
+            #pragma unroll
+            for (int w = 0; w < 4; ++w) { e[w] = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx); l_tot += e[w] * lw[w]; }
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const float lse_v = l_tot > 0.f ? (mx + __log2f(l_tot)) * kLn2 : -INFINITY;
+            const int h = sg.h0 + mr;
+            float acc[32];
+            #pragma unroll
+            for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+            #pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float ew = e[w] * inv;
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const f32x4 v = *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * 512 + dseg + 4 * j);
+                    acc[4 * j] += ew * v[0]; acc[4 * j + 1] += ew * v[1]; acc[4 * j + 2] += ew * v[2]; acc[4 * j + 3] += ew * v[3];
+                }
+            }
+            if (final_out) {
+                if (h < p.h_q) {
+                    uint16_t* op = p.o + (qrow0 + h) * kDv + dseg;
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        i16x8 w;
+                        #pragma unroll
+                        for (int e2 = 0; e2 < 8; ++e2) w[e2] = __builtin_bit_cast(short, (__bf16)acc[8 * j + e2]);
+                        *(i16x8*)(op + 8 * j) = w;
+                    }
+                    if ((tid & 15) == 0) p.lse[qrow0 + h] = lse_v;
+                }
+            } else {
+                float* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + dseg;
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) *(f32x4*)(wp + 4 * j) = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+                if ((tid & 15) == 0) p.ws_lse[(int64_t)sg.slot * RG + mr] = lse_v;
+            }
+            block_sync_lds();  // merge buffers are read before the next segment's DMA
+        }
+    }
+}
+
+template <bool FP8, bool SPARSE, int VAR>
+hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_kernel<FP8, SPARSE, VAR>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int variant, bool fp8, bool sparse, hipStream_t s) {
+    if (variant == kV128) {
+        if (fp8) return sparse ? launch_one<true, true, kV128>(p, s) : launch_one<true, false, kV128>(p, s);
+        return sparse ? launch_one<false, true, kV128>(p, s) : launch_one<false, false, kV128>(p, s);
+    }
+    if (fp8) return sparse ? launch_one<true, true, kV16>(p, s) : launch_one<true, false, kV16>(p, s);
+    return sparse ? launch_one<false, true, kV16>(p, s) : launch_one<false, false, kV16>(p, s);
+}
+
+}  // namespace mla

@@ -1,0 +1,134 @@
+"""Bit-exact properties of the HIP path: paging, gather and the masked-token set.
+
+The same metadata (same shapes) is used on both sides of every comparison,
+so the arithmetic order is identical and results must match bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+from workload import make_workload
+
+from tests.gpu_helpers import run_gpu, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu()
+
+
+def _same(a, b):
+    return torch.equal(_bits(a[0]), _bits(b[0])) and torch.equal(_bits(a[1]), _bits(b[1]))
+
+
+@pytest.mark.parametrize("fmt,h_q", [("bf16", 128), ("bf16", 16), ("fp8", 128), ("fp8", 16)])
+def test_page_shuffle_invariance(fmt, h_q):
+    say(f"page shuffle {fmt} h_q={h_q}")
+    w = make_workload(batch=3, s_q=1, h_q=h_q, seqlens=[700, 129, 64], kv_format=fmt, extra_blocks=5, seed=21)
+    base = run_gpu(w)
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(w.num_blocks, generator=g)  # page p moves to slot perm[p]
+    kv2 = torch.empty_like(w.kv)
+    kv2[perm] = w.kv
+    bt2 = torch.where(w.block_table >= 0, perm[w.block_table.clamp(min=0).long()].to(torch.int32), w.block_table)
+    w.kv, w.block_table = kv2, bt2
+    moved = run_gpu(w)
+    torch.cuda.synchronize()
+    assert _same(base, moved)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_gather_permutation_invariance(fmt):
+    say(f"gather permutation {fmt}")
+    w = make_workload(batch=2, s_q=1, h_q=128, kv_format=fmt, topk=300, sparse_tokens_per_seq=1024,
+                      invalid_frac=0.05, seed=22)
+    base = run_gpu(w)
+    g = torch.Generator().manual_seed(6)
+    n_rows = w.num_blocks * 64
+    perm = torch.randperm(n_rows, generator=g)          # row r moves to perm[r]
+    flat = w.kv.reshape(n_rows, -1)
+    moved = torch.empty_like(flat)
+    moved[perm] = flat
+    w.kv = moved.reshape(w.kv.shape)
+    idx = w.indices.long()
+    w.indices = torch.where(idx >= 0, perm[idx.clamp(min=0)], idx).to(torch.int32)
+    moved_out = run_gpu(w)
+    torch.cuda.synchronize()
+    assert _same(base, moved_out)
+
+
+def _poison_rows(w, keep_rows, value_bytes):
+    flat = w.kv.reshape(-1, w.kv.shape[2])
+    mask = torch.ones(flat.shape[0], dtype=torch.bool)
+    mask[keep_rows] = False
+    flat[mask] = value_bytes
+    return flat
+
+
+def _attended_rows(w):
+    rows = set()
+    for b in range(w.batch):
+        for i in range(w.s_q):
+            if w.indices is not None:
+                for v in w.indices[b, i].tolist():
+                    if 0 <= v < w.num_blocks * 64:
+                        rows.add(v)
+            else:
+                L = int(w.cache_seqlens[b])
+                lim = L - w.s_q + 1 + i if w.causal else L
+                for t in range(max(0, lim)):
+                    rows.add(int(w.block_table[b, t // 64]) * 64 + t % 64)
+    return torch.tensor(sorted(rows), dtype=torch.long)
+
+
+@pytest.mark.parametrize("fmt,h_q,causal,sparse", [("bf16", 128, False, False), ("bf16", 16, True, False),
+                                                  ("fp8", 128, True, False), ("fp8", 16, False, False),
+                                                  ("fp8", 128, False, True), ("bf16", 16, False, True)])
+def test_nan_poison_of_masked_rows(fmt, h_q, causal, sparse):
+    """Every row no query attends to (page tails, causal-excluded tokens,
+    unreferenced pages, rows named only by -1) is overwritten with NaN bytes;
+    o and lse must not change by a single bit."""
+    say(f"nan poison {fmt} h_q={h_q} causal={causal} sparse={sparse}")
+    if sparse:
+        w = make_workload(batch=2, s_q=1, h_q=h_q, kv_format=fmt, topk=150, sparse_tokens_per_seq=512,
+                          invalid_frac=0.1, seed=23)
+    else:
+        w = make_workload(batch=3, s_q=2 if causal else 1, h_q=h_q, seqlens=[301, 64, 5], kv_format=fmt,
+                          causal=causal, extra_blocks=4, seed=23)
+        # block_table padding points at a poisoned page instead of -1
+        w.block_table[w.block_table < 0] = w.num_blocks - 1
+    keep = _attended_rows(w)
+    w.kv = w.kv.clone()
+    flat = w.kv.reshape(-1, w.kv.shape[2])
+    zero = flat.clone()
+    zero_mask = torch.ones(flat.shape[0], dtype=torch.bool)
+    zero_mask[keep] = False
+    zero[zero_mask] = 0
+    w.kv = zero.reshape(w.kv.shape)
+    clean = run_gpu(w)
+    nan = zero.clone()
+    nan[zero_mask] = 0xFF  # 0xFFFF bf16 and 0xFF e4m3 are NaN; fp32 scale 0xFFFFFFFF is NaN
+    w.kv = nan.reshape(w.kv.shape)
+    poisoned = run_gpu(w)
+    torch.cuda.synchronize()
+    assert _same(clean, poisoned)
+    # conversely, changing an attended boundary token changes the output
+    last = keep[-1].item()
+    bumped = nan.clone()
+    bumped[last, :64] = 0x3C if fmt == "fp8" else 0x40
+    w.kv = bumped.reshape(w.kv.shape)
+    changed = run_gpu(w)
+    torch.cuda.synchronize()
+    assert not _same(poisoned, changed)
+
+
+def test_repeat_determinism():
+    say("repeat determinism x100")
+    w = make_workload(batch=4, s_q=1, h_q=128, seqlens=[3000, 10, 640, 1200], kv_format="bf16", seed=24)
+    g = to_gpu(w)
+    first = run_gpu(w, g)
+    torch.cuda.synchronize()
+    for _ in range(99):
+        again = run_gpu(w, g)
+        assert _same(first, again)

@@ -1,0 +1,73 @@
+"""mla_combine through the C ABI on hand-made partials vs the oracle's split merge."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_10_amd as mla
+from oracle import lse_merge
+
+from tests.gpu_helpers import LSE_RTOL, O_TOL, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("h_q,s_q", [(128, 1), (16, 2), (20, 1)])
+def test_combine_matches_oracle_merge(h_q, s_q):
+    say(f"combine h_q={h_q} s_q={s_q}")
+    dev = "cuda:0"
+    B, P = 3, 8
+    RG = 16 if h_q <= 64 else 128
+    n_hb = -(-h_q // RG)
+    n_rg = s_q * n_hb
+    Q = B * n_rg
+    rng = np.random.default_rng(h_q + s_q)
+    n_splits = rng.integers(0, 5, Q)
+    n_splits[0] = 3
+    if Q > 2:
+        n_splits[1] = 1
+        n_splits[2] = 0
+    offs = np.zeros(Q + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(n_splits)
+    S = Q + P
+    assert offs[-1] <= S
+    part_o = rng.standard_normal((S, RG, 512)).astype(np.float32)
+    part_lse = (rng.standard_normal((S, RG)) * 3).astype(np.float32)
+    part_lse[offs[0] + 1, :5] = -np.inf                     # an empty split
+    o_bytes = ((S * RG * 512 * 4 + 255) // 256) * 256
+    ws = torch.zeros(mla.workspace_size(B, s_q, h_q, P), dtype=torch.uint8, device=dev)
+    ws[:S * RG * 512 * 4] = torch.from_numpy(part_o.view(np.uint8).reshape(-1)).to(dev)
+    ws[o_bytes:o_bytes + S * RG * 4] = torch.from_numpy(part_lse.view(np.uint8).reshape(-1)).to(dev)
+    o = torch.full((B, s_q, h_q, 512), 7.0, dtype=torch.bfloat16, device=dev)   # sentinel
+    lse = torch.full((B, s_q, h_q), 7.0, dtype=torch.float32, device=dev)
+    q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((1, 64, 1152), dtype=torch.uint8, device=dev)
+    bt = torch.zeros((B, 1), dtype=torch.int32, device=dev)
+    seq = torch.zeros((B,), dtype=torch.int32, device=dev)
+    tm = torch.zeros((P, 8), dtype=torch.int32, device=dev)
+    so = torch.from_numpy(offs).to(dev)
+    a = mla.make_args(q, kv, bt, seq, tm, so, 0.1, False, False, None, ws, o, lse)
+    mla.mla_combine(a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    lg = lse.cpu().numpy()
+    for qq in range(Q):
+        b, rgi = divmod(qq, n_rg)
+        i, hb = divmod(rgi, n_hb)
+        n = n_splits[qq]
+        for r in range(RG):
+            h = hb * RG + r
+            if h >= h_q:
+                continue
+            if n == 1:
+                assert np.all(og[b, i, h] == 7.0) and lg[b, i, h] == 7.0   # left for the split kernel
+                continue
+            if n == 0:
+                assert np.all(og[b, i, h] == 0) and lg[b, i, h] == -np.inf
+                continue
+            sl = slice(offs[qq], offs[qq + 1])
+            ro, rl = lse_merge(part_o[sl, r].astype(np.float64), part_lse[sl, r].astype(np.float64))
+            assert np.max(np.abs(og[b, i, h] - ro)) <= O_TOL
+            assert abs(lg[b, i, h] - rl) <= LSE_RTOL * max(1.0, abs(rl))

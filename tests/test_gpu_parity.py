@@ -1,0 +1,97 @@
+"""HIP decode vs the float64 oracle on the same seeded inputs.
+
+Small cases are compared on every query row; the five full-size workloads are
+compared on sampled (b, i) rows that the oracle computes one by one, in the
+launch configuration the benchmark uses (metadata with the default number of
+parts, decode + combine)."""
+
+import numpy as np
+import pytest
+import torch
+
+from workload import config_workload, make_workload
+
+from tests.gpu_helpers import compare, oracle, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, rows=None, num_parts=None, label=None):
+    label = label or w.name
+    say(f"case: {label} num_parts={num_parts}")
+    o, lse, _, _ = run_gpu(w, num_parts=num_parts)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle(w, rows)
+    return compare(o, lse, o_ref, lse_ref, rows, label)
+
+
+SMALL = [
+    # (label, kwargs)
+    ("bf16 dense h128 ragged", dict(batch=3, s_q=1, h_q=128, seqlens=[1, 130, 700], kv_format="bf16")),
+    ("bf16 dense h16 ragged", dict(batch=4, s_q=1, h_q=16, seqlens=[64, 65, 1000, 3], kv_format="bf16")),
+    ("bf16 dense h4", dict(batch=2, s_q=1, h_q=4, seqlens=[256, 77], kv_format="bf16")),
+    ("bf16 dense h20 two head blocks", dict(batch=2, s_q=1, h_q=20, seqlens=[300, 129], kv_format="bf16")),
+    ("bf16 dense h100 padded rows", dict(batch=2, s_q=1, h_q=100, seqlens=[200, 513], kv_format="bf16")),
+    ("bf16 dense h130 two row groups", dict(batch=1, s_q=1, h_q=130, seqlens=[333], kv_format="bf16")),
+    ("bf16 dense empty sequence", dict(batch=3, s_q=1, h_q=128, seqlens=[0, 100, 0], kv_format="bf16")),
+    ("bf16 causal s_q=3", dict(batch=2, s_q=3, h_q=16, seqlens=[200, 2], kv_format="bf16", causal=True)),
+    ("bf16 causal s_q=2 h128", dict(batch=2, s_q=2, h_q=128, seqlens=[129, 64], kv_format="bf16", causal=True)),
+    ("fp8 dense h128", dict(batch=2, s_q=1, h_q=128, seqlens=[500, 64], kv_format="fp8")),
+    ("fp8 dense h16", dict(batch=3, s_q=1, h_q=16, seqlens=[1, 190, 640], kv_format="fp8")),
+    ("fp8 causal s_q=2 h128", dict(batch=3, s_q=2, h_q=128, seqlens=[1000, 65, 1], kv_format="fp8", causal=True)),
+    ("fp8 sparse h128", dict(batch=3, s_q=1, h_q=128, kv_format="fp8", topk=200, sparse_tokens_per_seq=1024,
+                             invalid_frac=0.05)),
+    ("fp8 sparse h16 s_q=2", dict(batch=2, s_q=2, h_q=16, kv_format="fp8", topk=130, sparse_tokens_per_seq=512,
+                                  invalid_frac=0.1)),
+    ("bf16 sparse h128", dict(batch=2, s_q=1, h_q=128, kv_format="bf16", topk=256, sparse_tokens_per_seq=2048,
+                              invalid_frac=0.05)),
+    ("bf16 sparse h4 mostly invalid", dict(batch=2, s_q=1, h_q=4, kv_format="bf16", topk=100,
+                                           sparse_tokens_per_seq=256, invalid_frac=0.95)),
+]
+
+
+@pytest.mark.parametrize("label,kw", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("num_parts", [None, 1, 7])
+def test_small_cases(label, kw, num_parts):
+    w = make_workload(seed=11, name=label, **kw)
+    _check(w, num_parts=num_parts, label=f"{label} parts={num_parts}")
+
+
+def test_sparse_all_invalid_rows():
+    w = make_workload(batch=2, s_q=1, h_q=128, kv_format="fp8", topk=64, sparse_tokens_per_seq=256,
+                      invalid_frac=0.0, seed=3, name="all -1")
+    w.indices[0] = -1
+    w.indices[1, 0, 5] = 10 ** 9        # out of range counts as unused
+    w.indices[1, 0, 6] = -7
+    _check(w, label="sparse all -1 / out of range")
+
+
+def test_config1_tiny():
+    _check(config_workload(1), label="config 1 (tiny dense)")
+
+
+def test_config2_dense_bf16_full():
+    w = config_workload(2)
+    _check(w, label="config 2 (dense bf16, all rows)")
+
+
+@pytest.mark.parametrize("L", [512, 2048, 16384])
+def test_config3_low_head(L):
+    w = config_workload(3, seqlen=L)
+    rows = [(0, 0), (7, 0), (15, 0)]
+    _check(w, rows=rows, label=f"config 3 L={L} (sampled rows)")
+
+
+def test_config3_64k_sampled():
+    w = config_workload(3, seqlen=65536)
+    _check(w, rows=[(3, 0), (12, 0)], label="config 3 L=65536 (sampled rows)")
+
+
+def test_config4_fp8_causal_sampled():
+    w = config_workload(4)
+    _check(w, rows=[(0, 0), (0, 1), (41, 1), (63, 0)], label="config 4 (fp8 causal, sampled rows)")
+
+
+def test_config5_sparse_fp8_sampled():
+    w = config_workload(5)
+    _check(w, rows=[(0, 0), (9, 0), (31, 0)], label="config 5 (sparse fp8, sampled rows)")
