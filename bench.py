@@ -194,17 +194,19 @@ def main():
 
     g_full = capture(G)
     # warmup
-    for gr in run_steps(args.warmup, g_full):
-        gr.replay()
+    with torch.cuda.stream(stream):
+        for gr in run_steps(args.warmup, g_full):
+            gr.replay()
     torch.cuda.synchronize()
     timed = run_steps(args.steps, g_full)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for gr in timed:
-        gr.replay()
-    e1.record(stream)
+    with torch.cuda.stream(stream):  # graph replays launch on the current stream
+        e0.record(stream)
+        for gr in timed:
+            gr.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms_wall = (t1 - t0) * 1e3 / args.steps
@@ -213,14 +215,15 @@ def main():
     # decode-kernel duration: same steps with the decode launch removed
     g_nodec = capture(G, with_decode=False)
     timed_nd = run_steps(args.steps, g_nodec, with_decode=False)
-    for gr in timed_nd[:2]:
-        gr.replay()
-    torch.cuda.synchronize()
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for gr in timed_nd:
-        gr.replay()
-    f1.record(stream)
+    with torch.cuda.stream(stream):
+        for gr in timed_nd[:2]:
+            gr.replay()
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for gr in timed_nd:
+            gr.replay()
+        f1.record(stream)
     torch.cuda.synchronize()
     rest_ms = f0.elapsed_time(f1) / args.steps
     decode_ms = max(step_ms - rest_ms, 1e-6)

@@ -81,10 +81,14 @@ int mla_metadata_size(int batch, int s_q, int h_q, int num_parts,
 
 /*
  * Bytes of fp32 split workspace mla_decode_with_kvcache needs. Layout, with
- * S = Q + num_parts slots: partial outputs fp32 [S][RG][512] (each already
- * divided by its own softmax sum), then, at the next 256-byte boundary,
- * partial lse fp32 [S][RG]. The slots of row-group sequence q are
- * split_offsets[q] .. split_offsets[q + 1] - 1, in KV order.
+ * S = Q + num_parts slots: partial outputs, S slots of RG x 512 fp32 (each
+ * already divided by its own softmax sum), then, at the next 256-byte
+ * boundary, partial lse fp32 [S][RG]. Inside a slot, RG = 16 is row-major
+ * [row][512]; RG = 128 is blocked as the split kernel's registers hold it:
+ * the float4 at index ((w * 16 + dd) * 4 + g) * 64 + lane holds row
+ * 32 w + (lane & 31), dims 32 dd + 8 g + 4 (lane >> 5) + 0..3. The slots of
+ * row-group sequence q are split_offsets[q] .. split_offsets[q + 1] - 1, in
+ * KV order.
  */
 int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes);
 
@@ -94,7 +98,7 @@ int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes
  *   cache_seqlens  device int32 [batch]; ignored when topk > 0 (may be NULL)
  *   topk           0 for dense attention, else the sparse index count
  *   num_parts      parts (workgroups) of the decode grid, 1..65535
- *   tile_meta      device int32 [num_parts][8], written: per part
+ *   tile_meta      device int32 [num_parts][8], 16-byte aligned, written: per part
  *                  {q_begin, t_begin, q_end, t_end (inclusive), first_split,
  *                   empty, 0, 0}
  *   split_offsets  device int32 [Q + 1], written: prefix sums of the number

@@ -31,6 +31,11 @@ COMMON_FLAGS = [
 ]
 
 
+# The decode kernel keeps MFMA accumulators of the score tile in VGPRs
+# (VGPR form) and pins the output accumulator to AGPRs with inline asm.
+EXTRA_FLAGS = {"mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -45,8 +50,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [hipcc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -160,6 +160,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
     if (topk < 0) return fail(MLA_ERR_INVALID, "topk must be >= 0 (got %d)", topk);
     if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
     if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
+    if (!aligned(tile_meta, 16)) return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned");
     const mla::Layout l = mla::layout_for(h_q, s_q);
     mla::MetaParams p;
     p.seqlens = cache_seqlens;

@@ -6,85 +6,139 @@
 // normalised (o_k = O_k / l_k) with lse_k = m_k + ln l_k, so the merge is
 // lse = ln sum_k e^{lse_k} and o = sum_k e^{lse_k - lse} o_k. Empty partials
 // (lse_k = -inf) weigh zero; a row with no partial at all gets o = 0 and
-// lse = -inf.
+// lse = -inf; a row with exactly one split was written by the split kernel.
 //
-// One wave per query row: lanes split the 512 output dims (8 each) and share
-// the reduction over splits through wave shuffles.
+// Workspace layout of one slot (RG rows x 512 dims, fp32):
+//   RG = 128: blocked as the split kernel's MFMA registers hold it, float4
+//     index ((w * 16 + dd) * 4 + g) * 64 + lane for row 32 w + (lane & 31),
+//     dims 32 dd + 8 g + 4 (lane >> 5) + 0..3;
+//   RG = 16: row-major [row][512].
+// Each thread owns one row and a fixed set of float4s; consecutive threads
+// read consecutive float4s of a slot.
 #include "mla_common.h"
 
 namespace mla {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 
-__device__ __forceinline__ float wave_max(float v) {
-    #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
+template <int RG>
+struct CombineMap {
+    // blocks per row-group sequence, float4s per thread per slot
+    static constexpr int kBlocksPerQ = RG == 128 ? 16 : 4;
+    static constexpr int kVec = RG == 128 ? 4 : 2;
+    // thread -> (row, float4 offsets within the slot, dims of each float4)
+    __device__ static void map(int blk, int t, int& row, int (&f4)[kVec], int (&dim)[kVec]) {
+        if constexpr (RG == 128) {
+            const int w = blk >> 2, dq = blk & 3;
+            const int lane = t & 63, g = (t >> 6) & 3;
+            row = 32 * w + (lane & 31);
+            #pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const int dd = 4 * dq + j;
+                f4[j] = ((w * 16 + dd) * 4 + g) * 64 + lane;
+                dim[j] = 32 * dd + 8 * g + 4 * (lane >> 5);
+            }
+        } else {
+            const int dq = blk;
+            row = t >> 4;
+            const int c = t & 15;
+            #pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                dim[j] = 128 * dq + 4 * c + 64 * j;
+                f4[j] = (row * 512 + dim[j]) >> 2;
+            }
+        }
+    }
+};
 
+template <int RG>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t rowg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int Q = p.batch * p.n_rg;
-    const int q = (int)(rowg / p.rg);
-    const int rr = (int)(rowg - (int64_t)q * p.rg);
-    if (q >= Q) return;
+    using M = CombineMap<RG>;
+    const int q = blockIdx.x / M::kBlocksPerQ;
+    const int blk = blockIdx.x - q * M::kBlocksPerQ;
     const int b = q / p.n_rg;
     const int rgi = q - b * p.n_rg;
     const int i = rgi / p.n_hb;
-    const int h = (rgi - i * p.n_hb) * p.rg + rr;
+    int row, f4[M::kVec], dim[M::kVec];
+    M::map(blk, threadIdx.x, row, f4, dim);
+    const int h = (rgi - i * p.n_hb) * RG + row;
     if (h >= p.h_q) return;
     const int s0 = p.split_offsets[q];
     const int n = p.split_offsets[q + 1] - s0;
     if (n == 1) return;  // the split kernel wrote the final row
     const int64_t orow = ((int64_t)b * p.s_q + i) * p.h_q + h;
-    uint16_t* op = p.o + orow * kDv + 8 * lane;
-    const float* lse_k = p.ws_lse + (int64_t)s0 * p.rg + rr;
-
+    uint16_t* op = p.o + orow * kDv;
+    const float* lse_k = p.ws_lse + (int64_t)s0 * RG + row;
+    const bool lse_writer = dim[0] == 0;  // exactly one thread per row holds dim 0
+    // max and sum of e^{lse_k - max} over the splits, 16 independent loads at a time
+    constexpr int kB = 16;
     float m = -INFINITY;
-    for (int k = lane; k < n; k += 64) m = fmaxf(m, lse_k[(int64_t)k * p.rg]);
-    m = wave_max(m);
+    for (int k0 = 0; k0 < n; k0 += kB) {
+        float lv[kB];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) lv[u] = (k0 + u < n) ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) m = fmaxf(m, lv[u]);
+    }
     if (n == 0 || m == -INFINITY) {
-        *(i16x8*)op = i16x8{};
-        if (lane == 0) p.lse[orow] = -INFINITY;
+        #pragma unroll
+        for (int j = 0; j < M::kVec; ++j) *(i16x4*)(op + dim[j]) = i16x4{};
+        if (lse_writer) p.lse[orow] = -INFINITY;
         return;
     }
     float s = 0.f;
-    for (int k = lane; k < n; k += 64) s += __expf(lse_k[(int64_t)k * p.rg] - m);
-    s = wave_sum(s);
-    const float lse = m + __logf(s);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float* ob = p.ws_o + ((int64_t)s0 * p.rg + rr) * kDv + 8 * lane;
-    for (int k = 0; k < n; ++k) {
-        const float lk = lse_k[(int64_t)k * p.rg];
-        if (lk == -INFINITY) continue;
-        const float w = __expf(lk - lse);
-        const float* src = ob + (int64_t)k * p.rg * kDv;
-        const f32x4 a = *(const f32x4*)src;
-        const f32x4 c = *(const f32x4*)(src + 4);
-        acc[0] += w * a[0]; acc[1] += w * a[1]; acc[2] += w * a[2]; acc[3] += w * a[3];
-        acc[4] += w * c[0]; acc[5] += w * c[1]; acc[6] += w * c[2]; acc[7] += w * c[3];
+    for (int k0 = 0; k0 < n; k0 += kB) {
+        float lv[kB];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) lv[u] = (k0 + u < n) ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) s += lv[u] == -INFINITY ? 0.f : __expf(lv[u] - m);
     }
-    i16x8 out;
+    const float lse = m + __logf(s);
+    f32x4 acc[M::kVec];
     #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = __builtin_bit_cast(short, (__bf16)acc[e]);
-    *(i16x8*)op = out;
-    if (lane == 0) p.lse[orow] = lse;
+    for (int j = 0; j < M::kVec; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4* base = (const f32x4*)(p.ws_o + (int64_t)s0 * RG * kDv);
+    constexpr int kSlot4 = RG * kDv / 4;  // float4s per slot
+    constexpr int kU = 8;                 // splits in flight
+    for (int k0 = 0; k0 < n; k0 += kU) {
+        float wgt[kU];
+        f32x4 v[kU][M::kVec];
+        #pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const bool in = k0 + u < n;
+            const float lk = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+            wgt[u] = lk == -INFINITY ? 0.f : __expf(lk - lse);
+            #pragma unroll
+            for (int j = 0; j < M::kVec; ++j)
+                v[u][j] = in ? base[(int64_t)(k0 + u) * kSlot4 + f4[j]] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        #pragma unroll
+        for (int u = 0; u < kU; ++u)
+            #pragma unroll
+            for (int j = 0; j < M::kVec; ++j) acc[j] += wgt[u] * v[u][j];
+    }
+    #pragma unroll
+    for (int j = 0; j < M::kVec; ++j) {
+        i16x4 o4;
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(short, (__bf16)acc[j][e]);
+        *(i16x4*)(op + dim[j]) = o4;
+    }
+    if (lse_writer) p.lse[orow] = lse;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
-    const int64_t rows = (int64_t)p.batch * p.n_rg * p.rg;
-    const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    const int Q = p.batch * p.n_rg;
+    if (p.rg == 128) {
+        hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)Q * CombineMap<128>::kBlocksPerQ), dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)Q * CombineMap<16>::kBlocksPerQ), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

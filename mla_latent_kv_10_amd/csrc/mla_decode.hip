@@ -134,6 +134,18 @@ __device__ __forceinline__ void scale_agpr(V& acc, float alpha) {
     }
 }
 
+
+// O += V^T P^T on the AGPR-resident accumulator (v_mfma_f32_32x32x16_bf16).
+// Inline asm pins the accumulator to AGPRs; the rest of the kernel's MFMAs
+// use VGPR accumulators. Hazards around this asm are covered explicitly:
+// callers separate it from VALU producers of its operands and from later
+// AGPR reads with s_nop (mfma_fence).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// >= 24 wait states: covers XDL-result -> VALU/accvgpr-read and VALU-write -> XDL-read hazards.
+__device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // ---------------------------------------------------------------- segment context
 
 struct Seg {
@@ -203,23 +215,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         const int64_t qrow0 = ((int64_t)sg.b * p.s_q + sg.i) * p.h_q;  // row index of head 0
         const int32_t* idx_row = SPARSE ? p.indices + ((int64_t)sg.b * p.s_q + sg.i) * p.topk : nullptr;
 
-        // Sparse: lane l holds the row of token l of a tile (kOOB when masked).
-        auto sparse_row = [&](int k) -> unsigned {
-            const int pos = k * kBlock + lane;
+        // Per-tile index prefetch, three tiles ahead of use, as one VMEM load per
+        // wave: sparse -> lane l holds the cache row of token l (kOOB when
+        // masked); dense -> every lane holds the tile's page id.
+        auto fetch_index = [&](int k) -> unsigned {
             unsigned r = kOOB;
-            if (k <= t1 && pos < p.topk) {
-                const int v = idx_row[pos];
-                r = (v >= 0 && v < p.num_rows) ? (unsigned)v : kOOB;
+            if (k <= t1) {
+                if (SPARSE) {
+                    const int pos = k * kBlock + lane;
+                    if (pos < p.topk) {
+                        const int v = idx_row[pos];
+                        r = (v >= 0 && v < p.num_rows) ? (unsigned)v : kOOB;
+                    }
+                } else {
+                    r = (unsigned)p.block_table[(int64_t)sg.b * p.mbps + k];
+                }
             }
             return r;
         };
         // Dense: row of token 0 of tile k, or -1 when the page id is invalid.
-        // Read through the constant address space so the uniform load is a
-        // scalar one (it does not count against vmcnt).
-        const int32_t __attribute__((address_space(4)))* bt_c =
-            (const int32_t __attribute__((address_space(4)))*)p.block_table;
-        auto dense_page_row0 = [&](int k) -> int {
-            const int blk = uniform(bt_c[(int64_t)sg.b * p.mbps + k]);
+        auto dense_page_row0 = [&](unsigned blk_bits) -> int {
+            const int blk = uniform((int)blk_bits);
             return (blk >= 0 && (int64_t)blk * kBlock < (int64_t)p.num_rows) ? blk * kBlock : -1;
         };
 
@@ -230,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             int page0 = 0, n_valid = 0;
             uint64_t mask;
             if (!SPARSE) {
-                page0 = dense_page_row0(k);
+                page0 = dense_page_row0(srow);
                 n_valid = min(kBlock, sg.limit - k * kBlock);
                 mask = (page0 < 0 || n_valid <= 0) ? 0ull : (n_valid >= 64 ? ~0ull : ((1ull << n_valid) - 1ull));
             } else {
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll 1
                 for (int c = wave; c < kRawUnits; c += 4) {
                     const int kk = c * 64 + lane;
-                    const int t = kk / kRawUnits;
+                    const int t = (kk * 1599) >> 16;  // kk / 41, exact for kk < 2624
                     const int u = kk - t * kRawUnits;
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
@@ -268,33 +284,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         };
         const int n_dma = FP8 ? (wave == 0 ? 11 : 10) : 18;
 
-        // Dequantise raw FP8 tile `raw` into the bf16 tile at `tile`.
+        // Dequantise raw FP8 tile `raw` into the bf16 tile at `tile`. Lane l
+        // handles token l; wave w handles raw latent units w, w+4, .., w+28
+        // (16 codes each, scale group = unit / 8) and rope units w, w+4.
+        // All LDS reads are issued before any conversion.
+        const int dq_x = (lane >> 1) & 7;  // swizzle of token `lane`
+        const int dq_base = ((lane >> 3) * 9 << 10) + ((lane & 7) << 7);
+        const int dq_c0 = (((2 * wave) ^ dq_x) & 7) << 4;      // unit 2*(w+4j) & 7 == 2w
+        const int dq_c1 = (((2 * wave + 1) ^ dq_x) & 7) << 4;
         auto dequant = [&](const char LDS_AS* raw, char LDS_AS* tile) {
-            // latent: 64 tokens x 32 raw units (16 codes each); lanes walk tokens
-            #pragma unroll 1
+            const char LDS_AS* rrow = raw + lane * kRawRow;
+            u32x4 c[8], rp[2];
+            #pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = *(const u32x4 LDS_AS*)(rrow + (wave + 4 * j) * 16);
+            const f32x4 sc4 = *(const f32x4 LDS_AS*)(rrow + 512);
+            #pragma unroll
+            for (int j = 0; j < 2; ++j) rp[j] = *(const u32x4 LDS_AS*)(rrow + 528 + (wave + 4 * j) * 16);
+            #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int item = tid + j * kThreads;
-                const int t = item & 63, pu = item >> 6;
-                const u32x4 c = *(const u32x4 LDS_AS*)(raw + t * kRawRow + pu * 16);
-                const float sc = *(const float LDS_AS*)(raw + t * kRawRow + 512 + (pu >> 3) * 4);
+                const float sc = sc4[j >> 1];  // unit w + 4j lies in scale group (w + 4j) / 8 == j / 2
                 float v[16];
                 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], false);
-                    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], true);
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[j][d], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[j][d], true);
                     v[4 * d + 0] = lo[0] * sc; v[4 * d + 1] = lo[1] * sc;
                     v[4 * d + 2] = hi[0] * sc; v[4 * d + 3] = hi[1] * sc;
                 }
-                *(bf16x8 LDS_AS*)(tile + tile_off(t, 2 * pu)) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
-                *(bf16x8 LDS_AS*)(tile + tile_off(t, 2 * pu + 1)) = pack8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+                char LDS_AS* dst = tile + dq_base + (j << 10);
+                *(bf16x8 LDS_AS*)(dst + dq_c0) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                *(bf16x8 LDS_AS*)(dst + dq_c1) = pack8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
             }
-            // rope: 64 tokens x 8 units of bf16, copied
-            #pragma unroll 1
+            #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int item = tid + j * kThreads;
-                const int t = item & 63, r = item >> 6;
-                const u32x4 c = *(const u32x4 LDS_AS*)(raw + t * kRawRow + 528 + r * 16);
-                *(u32x4 LDS_AS*)(tile + tile_off(t, 64 + r)) = c;
+                const int u = 64 + wave + 4 * j;
+                *(u32x4 LDS_AS*)(tile + dq_base + (8 << 10) + ((((u & 7) ^ dq_x) & 7) << 4)) = rp[j];
             }
         };
 
@@ -371,14 +395,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask) {
             if constexpr (VAR == kV128) {
                 f32x16 s0 = {}, s1 = {};
+                // K operands are read kPF k-steps ahead of their MFMAs so LDS
+                // latency hides under the MFMA chain.
+                constexpr int kPF = 2;
+                bf16x8 ka[kPF + 1][2];
+                #pragma unroll
+                for (int j = 0; j < kPF; ++j) {
+                    ka[j][0] = lds_read16(tile + koff[0][j & 3] + ((j >> 2) << 10));
+                    ka[j][1] = lds_read16(tile + koff[1][j & 3] + ((j >> 2) << 10));
+                }
                 #pragma unroll
                 for (int kk = 0; kk < 36; ++kk) {
-                    const int off = (kk >> 2) << 10;
-                    const bf16x8 a0 = lds_read16(tile + koff[0][kk & 3] + off);
-                    const bf16x8 a1 = lds_read16(tile + koff[1][kk & 3] + off);
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], s1, 0, 0, 0);
+                    const int nk = kk + kPF;
+                    if (nk < 36) {
+                        ka[nk % (kPF + 1)][0] = lds_read16(tile + koff[0][nk & 3] + ((nk >> 2) << 10));
+                        ka[nk % (kPF + 1)][1] = lds_read16(tile + koff[1][nk & 3] + ((nk >> 2) << 10));
+                    }
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][0], qreg[kk], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][1], qreg[kk], s1, 0, 0, 0);
                 }
+                // keep the read-ahead: reads first, then (2 MFMA, 2 reads) groups
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPF, 0);
+                #pragma unroll
+                for (int kk = 0; kk < 36 - kPF; ++kk) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPF, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 // lane holds row (lane&31), token 32*blk + 8*(v>>2) + 4*(lane>>5) + (v&3)
                 const int hh = lane >> 5;
@@ -401,10 +444,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if (__builtin_amdgcn_ballot_w64(need)) {
                     const float m_new = fmaxf(m_run, mt);
                     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                    l_run *= alpha;
-                    #pragma unroll
-                    for (int d = 0; d < 16; ++d) scale_agpr<f32x16, 16>(oacc[d], alpha);
-                    asm volatile("s_nop 2" ::: "memory");
+                    // rows with nothing accumulated yet hold O = 0: skip the scaling
+                    if (__builtin_amdgcn_ballot_w64(m_run != -INFINITY)) {
+                        l_run *= alpha;
+                        #pragma unroll
+                        for (int d = 0; d < 16; ++d) scale_agpr<f32x16, 16>(oacc[d], alpha);
+                        asm volatile("s_nop 2" ::: "memory");
+                    }
                     m_run = m_new;
                 }
                 const float mu = (m_run == -INFINITY) ? 0.f : m_run;
@@ -425,26 +471,54 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                                       s1[8 * c + 4], s1[8 * c + 5], s1[8 * c + 6], s1[8 * c + 7]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                // V operands (transposed reads) kVF MFMAs ahead.
+                constexpr int kVF = 3;
+                auto vread = [&](int n) -> bf16x8 {
+                    const int c = n >> 4, d = n & 15;
+                    const i16x4 lo = lds_read_tr(tile + voff[d & 1] + (((2 * c) * 9 + (d >> 1)) << 10));
+                    const i16x4 hi = lds_read_tr(tile + voff[2 + (d & 1)] + (((2 * c + 1) * 9 + (d >> 1)) << 10));
+                    const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    return __builtin_bit_cast(bf16x8, av);
+                };
+                bf16x8 va[kVF + 1];
                 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    #pragma unroll
-                    for (int d = 0; d < 16; ++d) {
-                        const int off_lo = ((2 * c) * 9 + (d >> 1)) << 10;
-                        const int off_hi = ((2 * c + 1) * 9 + (d >> 1)) << 10;
-                        const i16x4 lo = lds_read_tr(tile + voff[0 * 2 + (d & 1)] + off_lo);
-                        const i16x4 hi = lds_read_tr(tile + voff[1 * 2 + (d & 1)] + off_hi);
-                        const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[c], oacc[d], 0, 0, 0);
-                    }
+                for (int j = 0; j < kVF; ++j) va[j] = vread(j);
+                mfma_fence();  // pb (VALU) -> MFMA operand
+                #pragma unroll
+                for (int n = 0; n < 64; ++n) {
+                    if (n + kVF < 64) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
+                    const int c = n >> 4, d = n & 15;
+                    mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[c]);
                 }
+                mfma_fence();  // MFMA results -> later AGPR reads / scaling
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVF, 0);
+                #pragma unroll
+                for (int n = 0; n < 64 - kVF; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kVF, 0);
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 f32x4 s = {};
+                constexpr int kPF = 3;
+                bf16x8 ka[kPF + 1];
+                #pragma unroll
+                for (int j = 0; j < kPF; ++j) ka[j] = lds_read16(tile + koff[0][j & 1] + ((j >> 1) << 10));
                 #pragma unroll
                 for (int kk = 0; kk < 18; ++kk) {
-                    const bf16x8 a = lds_read16(tile + koff[0][kk & 1] + ((kk >> 1) << 10));
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[kk], s, 0, 0, 0);
+                    const int nk = kk + kPF;
+                    if (nk < 18) ka[nk % (kPF + 1)] = lds_read16(tile + koff[0][nk & 1] + ((nk >> 1) << 10));
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk % (kPF + 1)], qreg[kk], s, 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, kPF, 0);
+                #pragma unroll
+                for (int kk = 0; kk < 18 - kPF; ++kk) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kPF, 0);
+                __builtin_amdgcn_sched_barrier(0);
                 // lane holds row (lane&15), tokens 16*wave + 4*(lane>>4) + v
                 const int g = lane >> 4;
                 float x[4];
@@ -461,22 +535,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if (__builtin_amdgcn_ballot_w64(need)) {
                     const float m_new = fmaxf(m_run, mt);
                     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                    l_run *= alpha;
-                    #pragma unroll
-                    for (int d = 0; d < 32; ++d) scale_agpr<f32x4, 4>(oacc[d], alpha);
-                    asm volatile("s_nop 2" ::: "memory");
+                    if (__builtin_amdgcn_ballot_w64(m_run != -INFINITY)) {
+                        l_run *= alpha;
+                        #pragma unroll
+                        for (int d = 0; d < 32; ++d) scale_agpr<f32x4, 4>(oacc[d], alpha);
+                        asm volatile("s_nop 2" ::: "memory");
+                    }
                     m_run = m_new;
                 }
                 const float mu = (m_run == -INFINITY) ? 0.f : m_run;
                 #pragma unroll
                 for (int v = 0; v < 4; ++v) { x[v] = __builtin_amdgcn_exp2f(x[v] - mu); l_run += x[v]; }
                 const bf16x8 pb = pack8(x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f);
+                __builtin_amdgcn_sched_barrier(0);
+                constexpr int kVF = 4;
+                i16x4 va[kVF + 1];
+                #pragma unroll
+                for (int j = 0; j < kVF; ++j) va[j] = lds_read_tr(tile + voff[j & 3] + ((j >> 2) << 10));
                 #pragma unroll
                 for (int d = 0; d < 32; ++d) {
-                    const i16x4 lo = lds_read_tr(tile + voff[d & 3] + ((d >> 2) << 10));
+                    if (d + kVF < 32) va[(d + kVF) % (kVF + 1)] = lds_read_tr(tile + voff[(d + kVF) & 3] + (((d + kVF) >> 2) << 10));
+                    const i16x4 lo = va[d % (kVF + 1)];
                     const i16x8 av = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
                     oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[d], 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, kVF, 0);
+                #pragma unroll
+                for (int d = 0; d < 32 - kVF; ++d) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kVF, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
@@ -485,28 +575,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             char LDS_AS* stage0 = smem + (FP8 ? S::kRaw0 : S::kTileA);
             char LDS_AS* stage1 = smem + (FP8 ? S::kRaw1 : S::kTileB);
             char LDS_AS* ctile = smem + S::kTileA;  // FP8: the single bf16 tile
-            unsigned idx_a = kOOB, idx_b = kOOB, idx_c = kOOB;  // sparse rows of tiles k, k+1, k+2
-            if (SPARSE) {
-                idx_a = sparse_row(t0);
-                idx_b = sparse_row(t0 + 1);
-                idx_c = sparse_row(t0 + 2);
-            }
+            // index prefetch ring: tiles k, k+1, k+2
+            unsigned idx_a = fetch_index(t0), idx_b = fetch_index(t0 + 1), idx_c = fetch_index(t0 + 2);
             uint64_t mask_a = issue_tile(t0, stage0, idx_a), mask_b = 0;
             if (t0 + 1 <= t1) mask_b = issue_tile(t0 + 1, stage1, idx_b);
             for (int k = t0; k <= t1; ++k) {
                 const bool odd = ((k - t0) & 1) != 0;
                 char LDS_AS* cur = odd ? stage1 : stage0;
-                unsigned idx_d = kOOB;
-                if (SPARSE && k + 3 <= t1) idx_d = sparse_row(k + 3);
+                const unsigned idx_d = fetch_index(k + 3);
                 // VMEM instructions this wave issued after tile k's DMA (a
                 // lower bound is safe: it only waits longer).
                 int after = 0;
                 if (k + 1 <= t1) {
                     after += n_dma;
-                    if (SPARSE) {
-                        if (k > t0 && k + 2 <= t1) after += 1;
-                        if (k + 3 <= t1) after += 1;
-                    }
+                    if (k > t0 && k + 2 <= t1) after += 1;
+                    if (k + 3 <= t1) after += 1;
                 }
                 wait_vm(after);
                 block_sync_lds();
@@ -553,14 +636,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if (hh == 0) p.lse[qrow0 + h] = lse_v;
                 }
             } else {
-                float* wp = p.ws_o + ((int64_t)sg.slot * RG + rloc) * kDv;
+                // blocked partial layout: one 1 KB contiguous store per (d, g) per wave
+                f32x4* wp = (f32x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (wave * 16 * 4) * 64 + lane;
                 #pragma unroll
                 for (int d = 0; d < 16; ++d) {
                     #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int dim = 32 * d + 8 * g + 4 * hh;
                         f32x4 w = {oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv, oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv};
-                        *(f32x4*)(wp + dim) = w;
+                        wp[(d * 4 + g) * 64] = w;
                     }
                 }
                 if (hh == 0) p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
@@ -577,8 +660,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 *(f32x4 LDS_AS*)(mo + (wave * 16 + row) * 512 + 16 * d + 4 * g) = oacc[d];
             if (g == 0) { mm[wave * 16 + row] = m_run; mm[64 + wave * 16 + row] = l_w; }
             block_sync_lds();
-            const int mr = tid >> 4;           // row 0..15
-            const int dseg = (tid & 15) * 32;  // 32 dims per thread
+            // thread -> row mr, dims 4c + 64j (j = 0..7): 16 threads cover 64 contiguous dims
+            const int mr = tid >> 4;
+            const int c4 = (tid & 15) * 4;
             float mw[4], lw[4];
             float mx = -INFINITY;
             #pragma unroll
@@ -589,34 +673,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             const float lse_v = l_tot > 0.f ? (mx + __log2f(l_tot)) * kLn2 : -INFINITY;
             const int h = sg.h0 + mr;
-            float acc[32];
+            f32x4 acc[8];
             #pragma unroll
-            for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+            for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const float ew = e[w] * inv;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const f32x4 v = *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * 512 + dseg + 4 * j);
-                    acc[4 * j] += ew * v[0]; acc[4 * j + 1] += ew * v[1]; acc[4 * j + 2] += ew * v[2]; acc[4 * j + 3] += ew * v[3];
-                }
+                for (int j = 0; j < 8; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * 512 + c4 + 64 * j);
             }
             if (final_out) {
                 if (h < p.h_q) {
-                    uint16_t* op = p.o + (qrow0 + h) * kDv + dseg;
+                    uint16_t* op = p.o + (qrow0 + h) * kDv + c4;
                     #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        i16x8 w;
+                    for (int j = 0; j < 8; ++j) {
+                        i16x4 w4;
                         #pragma unroll
-                        for (int e2 = 0; e2 < 8; ++e2) w[e2] = __builtin_bit_cast(short, (__bf16)acc[8 * j + e2]);
-                        *(i16x8*)(op + 8 * j) = w;
+                        for (int e2 = 0; e2 < 4; ++e2) w4[e2] = __builtin_bit_cast(short, (__bf16)acc[j][e2]);
+                        *(i16x4*)(op + 64 * j) = w4;
                     }
                     if ((tid & 15) == 0) p.lse[qrow0 + h] = lse_v;
                 }
             } else {
-                float* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + dseg;
+                float* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + c4;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) *(f32x4*)(wp + 4 * j) = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+                for (int j = 0; j < 8; ++j) *(f32x4*)(wp + 64 * j) = acc[j];
                 if ((tid & 15) == 0) p.ws_lse[(int64_t)sg.slot * RG + mr] = lse_v;
             }
             block_sync_lds();  // merge buffers are read before the next segment's DMA

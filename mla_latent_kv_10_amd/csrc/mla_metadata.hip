@@ -5,37 +5,52 @@
 // workgroup of the decode grid) processes, and how many splits each
 // sequence has; every layer reuses the result. The rule (see include/mla.h):
 // units laid end to end, fixed_cost positions then one per tile, part =
-// floor(position / W). One workgroup computes it in parallel: two block
-// scans (positions, split counts), then a binary search per part.
+// floor(position / W). One workgroup of 1024 threads computes it: block-wide
+// exclusive scans built from wave shuffles (positions, last non-empty unit,
+// split counts), then a binary search per part.
 #include "mla_common.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kMT = 256;
+constexpr int kMT = 1024;
+constexpr int kWaves = kMT / 64;
 
-// Exclusive scan of vals[0..n) in place (LDS), returning the total. Each
-// thread owns one contiguous chunk; chunk sums are scanned by thread 0.
-__device__ int block_exclusive_scan(int* vals, int n, int* chunk_sums) {
-    const int tid = threadIdx.x;
-    const int per = (n + kMT - 1) / kMT;
-    const int b = tid * per;
-    const int e = min(n, b + per);
-    int s = 0;
-    for (int k = b; k < e; ++k) s += vals[k];
-    chunk_sums[tid] = s;
+enum ScanOp { kSum, kMax };
+
+template <ScanOp OP>
+__device__ __forceinline__ int combine(int a, int b) { return OP == kSum ? a + b : max(a, b); }
+
+// Exclusive scan of one value per thread across the workgroup (thread order);
+// `scratch` holds kWaves ints. *total receives the reduction over all threads.
+template <ScanOp OP>
+__device__ int block_exclusive_scan(int v, int identity, int* scratch, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = v;
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off, 64);
+        if (lane >= off) inc = combine<OP>(inc, u);
+    }
+    int exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = identity;
+    if (lane == 63) scratch[w] = inc;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int k = 0; k < kMT; ++k) { int v = chunk_sums[k]; chunk_sums[k] = run; run += v; }
-        chunk_sums[kMT] = run;
+    if (w == 0) {
+        int s = lane < kWaves ? scratch[lane] : identity;
+        #pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int u = __shfl_up(s, off, 64);
+            if (lane >= off) s = combine<OP>(s, u);
+        }
+        if (lane < kWaves) scratch[lane] = s;  // inclusive over waves
     }
     __syncthreads();
-    int run = chunk_sums[tid];
-    for (int k = b; k < e; ++k) { int v = vals[k]; vals[k] = run; run += v; }
+    const int before = w > 0 ? scratch[w - 1] : identity;
+    *total = scratch[kWaves - 1];
     __syncthreads();
-    return chunk_sums[kMT];
+    return combine<OP>(before, exc);
 }
 
 // Smallest q in [0, n) with cum[q + 1] > v (cum has n + 1 entries, non-decreasing).
@@ -49,63 +64,70 @@ __device__ int first_unit_past(const int* cum, int n, int v) {
 }
 
 __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
-    __shared__ int s_cum[kMaxUnits + 1];    // positions: exclusive scan of per-unit cost
+    __shared__ int s_cum[kMaxUnits + 1];    // exclusive scan of per-unit cost (positions)
     __shared__ int s_T[kMaxUnits];          // tiles per unit
     __shared__ int s_prev[kMaxUnits];       // last non-empty unit at or before q (-1 if none)
-    __shared__ int s_ns[kMaxUnits];         // splits per unit, then their exclusive prefix sums
-    __shared__ int s_chunk[kMT + 1];
+    __shared__ int s_scan[kWaves];
     const int Q = p.batch * p.n_rg;
     const int tid = threadIdx.x;
     const int C = p.fixed_cost;
+    const int per = (Q + kMT - 1) / kMT;    // <= 8 units per thread
+    const int b0 = tid * per, e0 = min(Q, b0 + per);
 
-    for (int q = tid; q < Q; q += kMT) {
+    // tiles and cost of this thread's (contiguous) units
+    int cost_sum = 0, last_ne = -1;
+    for (int q = b0; q < e0; ++q) {
         int T;
         if (p.topk > 0) {
             T = (p.topk + kBlock - 1) / kBlock;
         } else {
-            int L = p.seqlens[q / p.n_rg];
+            const int L = p.seqlens[q / p.n_rg];
             T = L > 0 ? (L + kBlock - 1) / kBlock : 0;
         }
         s_T[q] = T;
-        s_cum[q] = T > 0 ? C + T : 0;
+        cost_sum += T > 0 ? C + T : 0;
+        if (T > 0) last_ne = q;
     }
-    __syncthreads();
-    const int total = block_exclusive_scan(s_cum, Q, s_chunk);
-    if (tid == 0) s_cum[Q] = total;
-    // last non-empty unit at or before q, by a sequential pass over chunks
+    int total, unused;
+    const int cost_before = block_exclusive_scan<kSum>(cost_sum, 0, s_scan, &total);
+    const int ne_before = block_exclusive_scan<kMax>(last_ne, -1, s_scan, &unused);
     {
-        const int per = (Q + kMT - 1) / kMT;
-        const int b = tid * per, e = min(Q, b + per);
-        int last = -1;
-        for (int k = b; k < e; ++k) if (s_T[k] > 0) last = k;
-        s_chunk[tid] = last;
-        __syncthreads();
-        if (tid == 0) {
-            int run = -1;
-            for (int k = 0; k < kMT; ++k) { int v = s_chunk[k]; s_chunk[k] = run; if (v >= 0) run = v; }
+        int run = cost_before, prev = ne_before;
+        for (int q = b0; q < e0; ++q) {
+            s_cum[q] = run;
+            run += s_T[q] > 0 ? C + s_T[q] : 0;
+            if (s_T[q] > 0) prev = q;
+            s_prev[q] = prev;
         }
-        __syncthreads();
-        int run = s_chunk[tid];
-        for (int k = b; k < e; ++k) { if (s_T[k] > 0) run = k; s_prev[k] = run; }
-        __syncthreads();
+        if (tid == 0) s_cum[Q] = total;
     }
     int W = total > 0 ? (total + p.num_parts - 1) / p.num_parts : 1;
     W = max(W, max(p.min_payload, 1));
 
-    // split counts (distinct parts among a unit's tiles), then their prefix sums
-    for (int q = tid; q < Q; q += kMT) {
-        int T = s_T[q];
-        int ns = 0;
+    // split counts (distinct parts among a unit's tiles) and their prefix sums
+    int ns_sum = 0;
+    for (int q = b0; q < e0; ++q) {
+        const int T = s_T[q];
         if (T > 0) {
-            int x0 = s_cum[q] + C;
-            ns = (x0 + T - 1) / W - x0 / W + 1;
+            const int x0 = s_cum[q] + C;
+            ns_sum += (x0 + T - 1) / W - x0 / W + 1;
         }
-        s_ns[q] = ns;
     }
-    __syncthreads();
-    const int total_splits = block_exclusive_scan(s_ns, Q, s_chunk);
-    for (int q = tid; q < Q; q += kMT) p.split_offsets[q] = s_ns[q];
-    if (tid == 0) p.split_offsets[Q] = total_splits;
+    int total_splits;
+    const int ns_before = block_exclusive_scan<kSum>(ns_sum, 0, s_scan, &total_splits);
+    {
+        int run = ns_before;
+        for (int q = b0; q < e0; ++q) {
+            p.split_offsets[q] = run;
+            const int T = s_T[q];
+            if (T > 0) {
+                const int x0 = s_cum[q] + C;
+                run += (x0 + T - 1) / W - x0 / W + 1;
+            }
+        }
+        if (tid == 0) p.split_offsets[Q] = total_splits;
+    }
+    __syncthreads();  // s_cum / s_prev complete before the searches
 
     for (int part = tid; part < p.num_parts; part += kMT) {
         int32_t* out = p.tile_meta + (int64_t)part * 8;
@@ -133,7 +155,8 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
                 row[5] = 0;
             }
         }
-        for (int k = 0; k < 8; ++k) out[k] = row[k];
+        *(int4*)out = make_int4(row[0], row[1], row[2], row[3]);
+        *(int4*)(out + 4) = make_int4(row[4], row[5], row[6], row[7]);
     }
 }
 

@@ -14,6 +14,25 @@ from tests.gpu_helpers import LSE_RTOL, O_TOL, say
 pytestmark = pytest.mark.gpu
 
 
+def _slot_layout(part_o):
+    """Logical partials [S][RG][512] -> the documented workspace layout
+    (RG = 16 row-major; RG = 128 blocked: float4 ((w*16+dd)*4+g)*64+lane holds
+    row 32w+(lane&31), dims 32dd+8g+4(lane>>5)+0..3)."""
+    S, RG, _ = part_o.shape
+    if RG == 16:
+        return np.ascontiguousarray(part_o)
+    out = np.empty((S, 4, 16, 4, 64, 4), dtype=part_o.dtype)
+    for w in range(4):
+        for lane in range(64):
+            r = 32 * w + (lane & 31)
+            h = lane >> 5
+            for dd in range(16):
+                for g in range(4):
+                    d0 = 32 * dd + 8 * g + 4 * h
+                    out[:, w, dd, g, lane, :] = part_o[:, r, d0:d0 + 4]
+    return out.reshape(S, RG, 512)
+
+
 @pytest.mark.parametrize("h_q,s_q", [(128, 1), (16, 2), (20, 1)])
 def test_combine_matches_oracle_merge(h_q, s_q):
     say(f"combine h_q={h_q} s_q={s_q}")
@@ -38,7 +57,7 @@ def test_combine_matches_oracle_merge(h_q, s_q):
     part_lse[offs[0] + 1, :5] = -np.inf                     # an empty split
     o_bytes = ((S * RG * 512 * 4 + 255) // 256) * 256
     ws = torch.zeros(mla.workspace_size(B, s_q, h_q, P), dtype=torch.uint8, device=dev)
-    ws[:S * RG * 512 * 4] = torch.from_numpy(part_o.view(np.uint8).reshape(-1)).to(dev)
+    ws[:S * RG * 512 * 4] = torch.from_numpy(_slot_layout(part_o).view(np.uint8).reshape(-1)).to(dev)
     ws[o_bytes:o_bytes + S * RG * 4] = torch.from_numpy(part_lse.view(np.uint8).reshape(-1)).to(dev)
     o = torch.full((B, s_q, h_q, 512), 7.0, dtype=torch.bfloat16, device=dev)   # sentinel
     lse = torch.full((B, s_q, h_q), 7.0, dtype=torch.float32, device=dev)
