@@ -53,6 +53,58 @@ def algorithmic_counts(w):
     return pairs, int(L.sum()) * row_bytes
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.md")
+KERNEL_SOURCES = ("mla_decode.hip", "mla_common.h", "build.py")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the split kernel's sources and build flags (first 16 hex digits)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "mla_latent_kv_10_amd")
+    for name in KERNEL_SOURCES:
+        path = os.path.join(pkg, "csrc", name) if name != "build.py" else os.path.join(pkg, name)
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, num_parts: int):
+    """HBM bytes per split-kernel launch from the committed counter summary, or
+    None when there is none for this workload or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = kernel_source_hash()
+    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+        # machine-readable rows: "traffic | <workload> | <num_parts> | <bytes> | <source hash>"
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0] == "traffic" and cells[1] == workload and cells[2] == str(num_parts):
+            return int(cells[3]) if cells[4] == want else None
+    return None
+
+
+def copy_probe(mib: int, reps: int):
+    """A plain device copy of known size (counter calibration and the achievable-bandwidth figure)."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps + 1, "ms_per_copy": round(ms, 5),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1),
+                      "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
 def build_workload(args):
     from workload import config_workload
 
@@ -86,7 +138,7 @@ def cpu_baseline(w, seconds: float):
     n_rows = 0
     t0 = time.perf_counter()
     k = 0
-    while time.perf_counter() - t0 < seconds and k < 10 * len(rows):
+    while time.perf_counter() - t0 < seconds:
         b, i = rows[k % len(rows)]
         mla_decode_ref(q, kv, w.kv_format, block_table=bt, cache_seqlens=seq, softmax_scale=w.softmax_scale,
                        causal=w.causal, indices=idx, rows=[(b, i)])
@@ -114,6 +166,8 @@ def main():
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -124,6 +178,9 @@ def main():
 
     import mla_latent_kv_10_amd as mla
 
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     w = build_workload(args)
@@ -158,38 +215,35 @@ def main():
     L = mla.lib()
     import ctypes
 
-    def step(d, stream, with_decode=True):
+    def step(d, stream):
         sp = 0 if d["idx"] is not None else d["seq"].data_ptr()
         mla.check(L.mla_get_metadata(sp, w.batch, w.s_q, w.h_q, w.topk, num_parts, d["tm"].data_ptr(),
                                      d["so"].data_ptr(), stream))
-        if with_decode:
-            mla.check(L.mla_decode_with_kvcache(ctypes.byref(d["args"]), stream))
-        else:
-            mla.check(L.mla_combine(ctypes.byref(d["args"]), stream))
+        mla.check(L.mla_decode_with_kvcache(ctypes.byref(d["args"]), stream))
 
     stream = torch.cuda.Stream(device=dev)
     G = n_sets * max(1, 64 // n_sets)  # steps per graph replay
 
-    def capture(n_steps, with_decode=True):
+    def capture(n_steps):
         g = torch.cuda.CUDAGraph()
         # warm the path once outside capture
         with torch.cuda.stream(stream):
             for k in range(min(n_steps, n_sets)):
-                step(sets[k % n_sets], stream.cuda_stream, with_decode)
+                step(sets[k % n_sets], stream.cuda_stream)
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=stream):
             for k in range(n_steps):
-                step(sets[k % n_sets], torch.cuda.current_stream().cuda_stream, with_decode)
+                step(sets[k % n_sets], torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         return g
 
-    def run_steps(k_steps, full_g, with_decode=True):
+    def run_steps(k_steps, full_g):
         graphs = []
         reps, rem = divmod(k_steps, G)
         for _ in range(reps):
             graphs.append(full_g)
         if rem:
-            graphs.append(capture(rem, with_decode))
+            graphs.append(capture(rem))
         return graphs
 
     g_full = capture(G)
@@ -212,36 +266,45 @@ def main():
     step_ms_wall = (t1 - t0) * 1e3 / args.steps
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # decode-kernel duration: same steps with the decode launch removed
-    g_nodec = capture(G, with_decode=False)
-    timed_nd = run_steps(args.steps, g_nodec, with_decode=False)
+    # Split-kernel duration: a graph of mla_decode_splits launches alone (the
+    # metadata of each input set is already in place from the steps above),
+    # timed with events on the stream the graph launches on.
+    def capture_decode(n_launch):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(n_launch):
+                mla.check(L.mla_decode_splits(ctypes.byref(sets[k % n_sets]["args"]),
+                                              torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        return g
+
+    g_dec = capture_decode(G)
+    reps_dec = max(1, args.steps // G)
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for gr in timed_nd[:2]:
-            gr.replay()
+        g_dec.replay()
         torch.cuda.synchronize()
         f0.record(stream)
-        for gr in timed_nd:
-            gr.replay()
+        for _ in range(reps_dec):
+            g_dec.replay()
         f1.record(stream)
     torch.cuda.synchronize()
-    rest_ms = f0.elapsed_time(f1) / args.steps
-    decode_ms = max(step_ms - rest_ms, 1e-6)
+    decode_ms = f0.elapsed_time(f1) / (reps_dec * G)
 
     tflops = flops / (step_ms * 1e-3) / 1e12
     kv_gbps_step = kv_bytes / (step_ms * 1e-3) / 1e9
     kv_gbps_dec = kv_bytes / (decode_ms * 1e-3) / 1e9
-    ai = flops / max(kv_bytes + 2 * q_bytes, 1)
-    hbm_bound = ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    if hbm_bound:
+    ai = flops / max(kv_bytes, 1)
+    traffic = measured_traffic(w.name, num_parts)
+    if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         roof = {"bound": "hbm", "achieved": round(kv_gbps_dec, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(kv_gbps_dec / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(kv_gbps_dec / HBM_PEAK_GBPS, 4), "traffic": traffic}
     else:
         dec_tflops = flops / (decode_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "decode_kernel (split decode)"
-    roof["decode_ms"] = round(decode_ms, 5)
+                "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof["kernel"] = "decode_kernel (mla_decode_splits)"
+    roof["kernel_ms"] = round(decode_ms, 5)
     roof["per_launch"] = {"flop": flops, "kv_bytes": kv_bytes}
 
     out = {
@@ -268,6 +331,7 @@ def main():
         "kv_read_frac_hbm": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
         "tflops_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
         "ms_per_step_wall": round(step_ms_wall, 5),
+        "kernel_source_hash": kernel_source_hash(),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -55,14 +55,15 @@ extern "C" {
  * Split policy (the library's own rule; the pages give the metadata's role,
  * [Walkthrough] §七 "split-KV", but no format):
  *   Query rows are grouped into "row groups" of RG heads of one query
- *   position: RG = 16 when h_q <= 64, else RG = 128. A row-group sequence
- *   q = b * n_rg + i * n_hb + hb, with n_hb = ceil(h_q / RG) head blocks and
+ *   position: RG = 16 when h_q <= 16, RG = 64 when 16 < h_q <= 64, else
+ *   RG = 128. A row-group sequence q = b * n_rg + i * n_hb + hb, with
+ *   n_hb = ceil(h_q / RG) head blocks and
  *   n_rg = s_q * n_hb, covers T_q = ceil(L_b / 64) tiles of 64 tokens (dense)
  *   or ceil(topk / 64) tiles (sparse). Units are laid end to end, each
  *   non-empty one first taking FIXED_COST positions, then one per tile; with
  *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
  *   MIN_PAYLOAD), the tile at position x goes to part floor(x / W).
- *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 2; RG 16 -> 1 and 1.
+ *   FIXED_COST and MIN_PAYLOAD: RG 128 or 64 -> 2 and 2; RG 16 -> 1 and 1.
  */
 
 /* Message for the last non-OK status on this thread ("" if none). */
@@ -84,7 +85,7 @@ int mla_metadata_size(int batch, int s_q, int h_q, int num_parts,
  * S = Q + num_parts slots: partial outputs, S slots of RG x 512 fp32 (each
  * already divided by its own softmax sum), then, at the next 256-byte
  * boundary, partial lse fp32 [S][RG]. Inside a slot, RG = 16 is row-major
- * [row][512]; RG = 128 is blocked as the split kernel's registers hold it:
+ * [row][512]; RG = 128 and 64 are blocked as the split kernel's registers hold it:
  * the float4 at index ((w * 16 + dd) * 4 + g) * 64 + lane holds row
  * 32 w + (lane & 31), dims 32 dd + 8 g + 4 (lane >> 5) + 0..3. The slots of
  * row-group sequence q are split_offsets[q] .. split_offsets[q + 1] - 1, in
@@ -156,6 +157,16 @@ typedef struct mla_decode_args {
  * MLA_ERR_UNSUPPORTED, MLA_ERR_HIP.
  */
 int mla_decode_with_kvcache(const mla_decode_args* args, void* stream);
+
+/*
+ * The split kernel of mla_decode_with_kvcache alone: each part attends its
+ * tile ranges ([Walkthrough] §七, split-KV). Rows of a sequence with a
+ * single split are finished (o, lse); the others leave fp32 partials in the
+ * workspace for mla_combine, which must follow on the same stream with the
+ * same arguments before o and lse are read. Lets a caller place work between
+ * the two kernels. Same arguments and errors as mla_decode_with_kvcache.
+ */
+int mla_decode_splits(const mla_decode_args* args, void* stream);
 
 /*
  * Split-KV LSE merge ([Walkthrough] §七: m = max m_k,

@@ -71,6 +71,7 @@ EXPORTS = (
     "mla_workspace_size",
     "mla_get_metadata",
     "mla_decode_with_kvcache",
+    "mla_decode_splits",
     "mla_combine",
 )
 
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
     L.mla_get_metadata.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.mla_decode_with_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    L.mla_decode_splits.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     for name in EXPORTS:
         getattr(L, name).restype = ctypes.c_char_p if name == "mla_last_error" else ctypes.c_int
@@ -233,6 +235,11 @@ def mla_decode_with_kvcache(q, kv, block_table, cache_seqlens, head_dim_v: int, 
                   is_fp8_kvcache, indices, workspace, o, lse)
     check(lib().mla_decode_with_kvcache(ctypes.byref(a), _stream_handle(q.device)))
     return o, lse
+
+
+def mla_decode_splits(args: MlaDecodeArgs, stream: int) -> None:
+    """Run only the split kernel for a prepared argument block (mla_combine must follow)."""
+    check(lib().mla_decode_splits(ctypes.byref(args), stream))
 
 
 def mla_combine(args: MlaDecodeArgs, stream: int) -> None:

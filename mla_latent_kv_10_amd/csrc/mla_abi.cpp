@@ -34,7 +34,7 @@ int check_shape(int batch, int s_q, int h_q, int num_parts) {
     if (h_q < 1) return fail(MLA_ERR_INVALID, "h_q must be >= 1 (got %d)", h_q);
     if (num_parts < 1 || num_parts > 65535)
         return fail(MLA_ERR_INVALID, "num_parts must be in [1, 65535] (got %d)", num_parts);
-    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
     const int64_t Q = (int64_t)batch * l.n_rg;
     if (Q > mla::kMaxUnits)
         return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * ceil(h_q / %d) = %lld exceeds %d row-group sequences",
@@ -43,7 +43,7 @@ int check_shape(int batch, int s_q, int h_q, int num_parts) {
 }
 
 size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
-    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
     const size_t slots = (size_t)batch * l.n_rg + (size_t)num_parts;
     const size_t o_bytes = slots * l.rg * mla::kDv * sizeof(float);
     const size_t lse_bytes = slots * l.rg * sizeof(float);
@@ -89,7 +89,7 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (a->workspace_bytes < need)
         return fail(MLA_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", a->workspace_bytes, need);
 
-    const mla::Layout l = mla::layout_for(a->h_q, a->s_q);
+    const mla::Layout l = mla::layout_for(a->h_q, a->s_q, a->batch, a->num_parts);
     const size_t slots = (size_t)a->batch * l.n_rg + (size_t)a->num_parts;
     const size_t o_bytes = ((slots * l.rg * mla::kDv * sizeof(float)) + 255) & ~(size_t)255;
     p->q = static_cast<const uint16_t*>(a->q);
@@ -139,7 +139,7 @@ int mla_metadata_size(int batch, int s_q, int h_q, int num_parts, int64_t* tile_
     if (!tile_meta_elems || !split_offsets_elems) return fail(MLA_ERR_INVALID, "output pointers are NULL");
     int st = check_shape(batch, s_q, h_q, num_parts);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
     *tile_meta_elems = (int64_t)num_parts * 8;
     *split_offsets_elems = (int64_t)batch * l.n_rg + 1;
     return ok();
@@ -161,7 +161,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
     if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
     if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
     if (!aligned(tile_meta, 16)) return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned");
-    const mla::Layout l = mla::layout_for(h_q, s_q);
+    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
     mla::MetaParams p;
     p.seqlens = cache_seqlens;
     p.tile_meta = tile_meta;
@@ -181,12 +181,23 @@ int mla_decode_with_kvcache(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = prepare(args, &p);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(args->h_q, args->s_q);
+    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = mla::launch_decode(p, l.variant, args->kv_format == MLA_KV_FP8_656, args->indices != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     e = mla::launch_combine(p, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_decode_splits(const mla_decode_args* args, void* stream) {
+    mla::DecodeParams p;
+    int st = prepare(args, &p);
+    if (st) return st;
+    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
+    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format == MLA_KV_FP8_656, args->indices != nullptr,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -9,7 +9,7 @@
 // lse = -inf; a row with exactly one split was written by the split kernel.
 //
 // Workspace layout of one slot (RG rows x 512 dims, fp32):
-//   RG = 128: blocked as the split kernel's MFMA registers hold it, float4
+//   RG = 128 or 64: blocked as the split kernel's MFMA registers hold it, float4
 //     index ((w * 16 + dd) * 4 + g) * 64 + lane for row 32 w + (lane & 31),
 //     dims 32 dd + 8 g + 4 (lane >> 5) + 0..3;
 //   RG = 16: row-major [row][512].
@@ -26,11 +26,11 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 template <int RG>
 struct CombineMap {
     // blocks per row-group sequence, float4s per thread per slot
-    static constexpr int kBlocksPerQ = RG == 128 ? 16 : 4;
-    static constexpr int kVec = RG == 128 ? 4 : 2;
+    static constexpr int kBlocksPerQ = RG == 16 ? 4 : RG / 8;  // 128 -> 16, 64 -> 8
+    static constexpr int kVec = RG == 16 ? 2 : 4;
     // thread -> (row, float4 offsets within the slot, dims of each float4)
     __device__ static void map(int blk, int t, int& row, int (&f4)[kVec], int (&dim)[kVec]) {
-        if constexpr (RG == 128) {
+        if constexpr (RG != 16) {
             const int w = blk >> 2, dq = blk & 3;
             const int lane = t & 63, g = (t >> 6) & 3;
             row = 32 * w + (lane & 31);
@@ -136,6 +136,8 @@ hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
     const int Q = p.batch * p.n_rg;
     if (p.rg == 128) {
         hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)Q * CombineMap<128>::kBlocksPerQ), dim3(256), 0, s, p);
+    } else if (p.rg == 64) {
+        hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)Q * CombineMap<64>::kBlocksPerQ), dim3(256), 0, s, p);
     } else {
         hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)Q * CombineMap<16>::kBlocksPerQ), dim3(256), 0, s, p);
     }

@@ -22,7 +22,7 @@ constexpr int kRawTileBytes = kBlock * kRawRow; // one FP8 tile as stored, 41 x 
 constexpr int kMaxUnits = 8192;     // row-group sequences per call (metadata LDS)
 constexpr int kThreads = 256;       // four wave64s per workgroup
 
-enum Variant { kV128 = 0, kV16 = 1 };
+enum Variant { kV128 = 0, kV16 = 1, kV64 = 2 };
 
 // Row-group policy; it is part of the ABI contract (see include/mla.h).
 struct Layout {
@@ -34,10 +34,20 @@ struct Layout {
     int variant;
 };
 
-inline Layout layout_for(int h_q, int s_q) {
+// h_q <= 16: one 16-head group per query position, four waves splitting each
+// tile's tokens. 16 < h_q <= 64: 64-head groups (two row waves x two token
+// waves). h_q > 64: 128-head groups (four row waves, every token).
+inline Layout layout_for(int h_q, int s_q, int batch, int num_parts) {
+    (void)batch;
+    (void)num_parts;
     Layout l;
-    if (h_q <= 64) { l.rg = 16; l.fixed_cost = 1; l.min_payload = 1; l.variant = kV16; }
-    else           { l.rg = 128; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV128; }
+    if (h_q <= 16) {
+        l.rg = 16; l.fixed_cost = 1; l.min_payload = 1; l.variant = kV16;
+    } else if (h_q <= 64) {
+        l.rg = 64; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV64;
+    } else {
+        l.rg = 128; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV128;
+    }
     l.n_hb = (h_q + l.rg - 1) / l.rg;
     l.n_rg = s_q * l.n_hb;
     return l;

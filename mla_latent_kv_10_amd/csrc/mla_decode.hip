@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     const __amdgpu_buffer_rsrc_t kv_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)p.row_bytes, p.num_rows, 0x00020000);
 
-    constexpr int RG = (VAR == kV128) ? 128 : 16;
+    constexpr int RG = (VAR == kV128) ? 128 : (VAR == kV64 ? 64 : 16);
 
     for (int qq = qb; qq <= qe; ++qq) {
         Seg sg;
@@ -324,11 +324,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
         // ------------------------------------------------ compute state
         // V128: wave owns rows 32*wave + (lane & 31); all 64 tokens of a tile.
+        // V64 : wave owns rows 32*rw + (lane & 31) and tokens 32*tw .. +31 of
+        //       each tile (rw = wave >> 1, tw = wave & 1).
         // V16 : wave owns tokens 16*wave .. +15 of each tile; all 16 rows.
-        constexpr int NQ = (VAR == kV128) ? 36 : 18;   // k-steps over 576 dims
-        constexpr int NO = (VAR == kV128) ? 16 : 32;   // output blocks over 512 dims
+        constexpr bool R32 = VAR != kV16;               // 32 rows per wave, 32x32x16 MFMA
+        constexpr int NB = (VAR == kV128) ? 2 : 1;      // 32-token blocks per wave per tile
+        const int rw = (VAR == kV64) ? (wave >> 1) : wave;
+        const int tw = (VAR == kV64) ? (wave & 1) : 0;
+        constexpr int NQ = R32 ? 36 : 18;   // k-steps over 576 dims
+        constexpr int NO = R32 ? 16 : 32;   // output blocks over 512 dims
         bf16x8 qreg[NQ];
-        typedef typename std::conditional<VAR == kV128, f32x16, f32x4>::type Acc;
+        typedef typename std::conditional<R32, f32x16, f32x4>::type Acc;
         Acc oacc[NO];
         #pragma unroll
         for (int d = 0; d < NO; ++d) oacc[d] = Acc{};
@@ -337,14 +343,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
         {
             int row, dsub;
-            if constexpr (VAR == kV128) { row = 32 * wave + (lane & 31); dsub = 8 * (lane >> 5); }
+            if constexpr (R32) { row = 32 * rw + (lane & 31); dsub = 8 * (lane >> 5); }
             else { row = lane & 15; dsub = 8 * (lane >> 4); }
             const int h = sg.h0 + row;
             const bool ok = h < p.h_q;
             const uint16_t* qp = p.q + (qrow0 + (ok ? h : 0)) * kDqk + dsub;
             #pragma unroll
             for (int kk = 0; kk < NQ; ++kk) {
-                const int dim0 = (VAR == kV128) ? 16 * kk : 32 * kk;
+                const int dim0 = R32 ? 16 * kk : 32 * kk;
                 i16x8 v = *(const i16x8*)(qp + dim0);
                 if (!ok) v = i16x8{};
                 qreg[kk] = __builtin_bit_cast(bf16x8, v);
@@ -352,13 +358,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
 
         // Per-lane LDS offsets (see the layout derivation in the comments).
-        int koff[2][4];   // V128: [token block][k-step & 3]; V16 uses koff[0][0..1]
-        int voff[4];      // V128: [lohi*2 + (d&1)]; V16: [d&3]
-        if constexpr (VAR == kV128) {
+        int koff[2][4];   // 32-row variants: [token block][k-step & 3]; V16 uses koff[0][0..1]
+        int voff[4];      // 32-row variants: [lohi*2 + (d&1)]; V16: [d&3]
+        if constexpr (R32) {
             const int hh = lane >> 5;
             #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int t = 32 * blk + (lane & 31);
+            for (int blk = 0; blk < NB; ++blk) {
+                const int t = 32 * (VAR == kV128 ? blk : tw) + (lane & 31);
                 const int base = ((t >> 3) * 9 << 10) + ((t & 7) << 7);
                 const int x = (t >> 1) & 7;
                 #pragma unroll
@@ -393,52 +399,63 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
         // ------------------------------------------------ compute one tile
         auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask) {
-            if constexpr (VAR == kV128) {
-                f32x16 s0 = {}, s1 = {};
-                // K operands are read kPF k-steps ahead of their MFMAs so LDS
-                // latency hides under the MFMA chain.
-                constexpr int kPF = 2;
-                bf16x8 ka[kPF + 1][2];
+            if constexpr (R32) {
+                // S^T = K Q^T on 32x32x16 MFMAs: two accumulation chains (the two
+                // token blocks for V128; even/odd k-steps of the one block for V64).
+                f32x16 sc[2] = {f32x16{}, f32x16{}};
+                constexpr int kPF = (NB == 2) ? 2 : 4;
+                bf16x8 ka[kPF + 1][NB];
                 #pragma unroll
-                for (int j = 0; j < kPF; ++j) {
-                    ka[j][0] = lds_read16(tile + koff[0][j & 3] + ((j >> 2) << 10));
-                    ka[j][1] = lds_read16(tile + koff[1][j & 3] + ((j >> 2) << 10));
-                }
+                for (int j = 0; j < kPF; ++j)
+                    #pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) ka[j][bb] = lds_read16(tile + koff[bb][j & 3] + ((j >> 2) << 10));
                 #pragma unroll
                 for (int kk = 0; kk < 36; ++kk) {
                     const int nk = kk + kPF;
                     if (nk < 36) {
-                        ka[nk % (kPF + 1)][0] = lds_read16(tile + koff[0][nk & 3] + ((nk >> 2) << 10));
-                        ka[nk % (kPF + 1)][1] = lds_read16(tile + koff[1][nk & 3] + ((nk >> 2) << 10));
+                        #pragma unroll
+                        for (int bb = 0; bb < NB; ++bb)
+                            ka[nk % (kPF + 1)][bb] = lds_read16(tile + koff[bb][nk & 3] + ((nk >> 2) << 10));
                     }
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][0], qreg[kk], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][1], qreg[kk], s1, 0, 0, 0);
+                    #pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int ch = (NB == 2) ? bb : (kk & 1);
+                        sc[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][bb], qreg[kk], sc[ch], 0, 0, 0);
+                    }
                 }
-                // keep the read-ahead: reads first, then (2 MFMA, 2 reads) groups
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPF, 0);
+                // keep the read-ahead: reads first, then (NB MFMA, NB reads) groups
+                __builtin_amdgcn_sched_group_barrier(0x100, NB * kPF, 0);
                 #pragma unroll
                 for (int kk = 0; kk < 36 - kPF; ++kk) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPF, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NB * kPF, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                // lane holds row (lane&31), token 32*blk + 8*(v>>2) + 4*(lane>>5) + (v&3)
+                if constexpr (NB == 1) sc[0] += sc[1];
+                // lane holds row (lane&31), token 32*tb + 8*(v>>2) + 4*(lane>>5) + (v&3)
                 const int hh = lane >> 5;
                 #pragma unroll
-                for (int v = 0; v < 16; ++v) { s0[v] *= p.scale_log2; s1[v] *= p.scale_log2; }
+                for (int bb = 0; bb < NB; ++bb)
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) sc[bb][v] *= p.scale_log2;
                 if (mask != ~0ull) {
                     const uint64_t mh = mask >> (4 * hh);
                     #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int t = 8 * (v >> 2) + (v & 3);
-                        if (!((mh >> t) & 1ull)) s0[v] = -INFINITY;
-                        if (!((mh >> (32 + t)) & 1ull)) s1[v] = -INFINITY;
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int tb = (VAR == kV128) ? bb : tw;
+                        #pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int t = 32 * tb + 8 * (v >> 2) + (v & 3);
+                            if (!((mh >> t) & 1ull)) sc[bb][v] = -INFINITY;
+                        }
                     }
                 }
-                float mt = fmaxf(s0[0], s1[0]);
+                float mt = sc[0][0];
                 #pragma unroll
-                for (int v = 1; v < 16; ++v) mt = fmaxf(mt, fmaxf(s0[v], s1[v]));
+                for (int bb = 0; bb < NB; ++bb)
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sc[bb][v]);
                 mt = fmaxf(mt, wave_shfl_xor(mt, 32));
                 const bool need = mt > m_run + kLazyMax;
                 if (__builtin_amdgcn_ballot_w64(need)) {
@@ -456,25 +473,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const float mu = (m_run == -INFINITY) ? 0.f : m_run;
                 float ps = 0.f;
                 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    s0[v] = __builtin_amdgcn_exp2f(s0[v] - mu);
-                    s1[v] = __builtin_amdgcn_exp2f(s1[v] - mu);
-                    ps += s0[v] + s1[v];
-                }
+                for (int bb = 0; bb < NB; ++bb)
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        sc[bb][v] = __builtin_amdgcn_exp2f(sc[bb][v] - mu);
+                        ps += sc[bb][v];
+                    }
                 l_run += ps;
-                bf16x8 pb[4];
+                bf16x8 pb[2 * NB];
                 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    pb[c] = pack8(s0[8 * c + 0], s0[8 * c + 1], s0[8 * c + 2], s0[8 * c + 3],
-                                  s0[8 * c + 4], s0[8 * c + 5], s0[8 * c + 6], s0[8 * c + 7]);
-                    pb[2 + c] = pack8(s1[8 * c + 0], s1[8 * c + 1], s1[8 * c + 2], s1[8 * c + 3],
-                                      s1[8 * c + 4], s1[8 * c + 5], s1[8 * c + 6], s1[8 * c + 7]);
-                }
+                for (int bb = 0; bb < NB; ++bb)
+                    #pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        pb[2 * bb + c] = pack8(sc[bb][8 * c + 0], sc[bb][8 * c + 1], sc[bb][8 * c + 2], sc[bb][8 * c + 3],
+                                               sc[bb][8 * c + 4], sc[bb][8 * c + 5], sc[bb][8 * c + 6], sc[bb][8 * c + 7]);
                 __builtin_amdgcn_sched_barrier(0);
-                // V operands (transposed reads) kVF MFMAs ahead.
+                // V operands (transposed reads) kVF MFMAs ahead; c = the tile's 16-token chunk
                 constexpr int kVF = 3;
+                constexpr int NPV = 32 * NB;
                 auto vread = [&](int n) -> bf16x8 {
-                    const int c = n >> 4, d = n & 15;
+                    const int cl = n >> 4, d = n & 15;
+                    const int c = (VAR == kV128) ? cl : 2 * tw + cl;
                     const i16x4 lo = lds_read_tr(tile + voff[d & 1] + (((2 * c) * 9 + (d >> 1)) << 10));
                     const i16x4 hi = lds_read_tr(tile + voff[2 + (d & 1)] + (((2 * c + 1) * 9 + (d >> 1)) << 10));
                     const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -485,15 +504,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 for (int j = 0; j < kVF; ++j) va[j] = vread(j);
                 mfma_fence();  // pb (VALU) -> MFMA operand
                 #pragma unroll
-                for (int n = 0; n < 64; ++n) {
-                    if (n + kVF < 64) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
-                    const int c = n >> 4, d = n & 15;
-                    mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[c]);
+                for (int n = 0; n < NPV; ++n) {
+                    if (n + kVF < NPV) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
+                    const int cl = n >> 4, d = n & 15;
+                    mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[cl]);
                 }
                 mfma_fence();  // MFMA results -> later AGPR reads / scaling
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVF, 0);
                 #pragma unroll
-                for (int n = 0; n < 64 - kVF; ++n) {
+                for (int n = 0; n < NPV - kVF; ++n) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
@@ -612,11 +631,45 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
         // ------------------------------------------------ epilogue
         const bool final_out = sg.n_splits == 1;
-        if constexpr (VAR == kV128) {
+        if constexpr (VAR == kV64) {
+            // token-half 1 hands (m, l, O) to token-half 0 of the same rows
+            float LDS_AS* xo = (float LDS_AS*)smem;                          // [2][16][4][64] float4
+            float LDS_AS* xm = (float LDS_AS*)(smem + 2 * 16 * 4 * 64 * 16);  // [2][64] m, then [2][64] l
+            if (tw == 1) {
+                #pragma unroll
+                for (int d = 0; d < 16; ++d)
+                    #pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4) =
+                            f32x4{oacc[d][4 * g], oacc[d][4 * g + 1], oacc[d][4 * g + 2], oacc[d][4 * g + 3]};
+                xm[rw * 64 + lane] = m_run;
+                xm[128 + rw * 64 + lane] = l_run;
+            }
+            block_sync_lds();
+            if (tw == 0) {
+                const float m1 = xm[rw * 64 + lane], l1 = xm[128 + rw * 64 + lane];
+                const float mx = fmaxf(m_run, m1);
+                const float e0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                const float e1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+                #pragma unroll
+                for (int d = 0; d < 16; ++d)
+                    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v = *(const f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4);
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) oacc[d][4 * g + e] = oacc[d][4 * g + e] * e0 + v[e] * e1;
+                    }
+                l_run = l_run * e0 + l1 * e1;
+                m_run = mx;
+            }
+            block_sync_lds();  // merge buffer read before the next segment's DMA
+        }
+        if constexpr (R32) {
+          if (VAR == kV128 || tw == 0) {
             const float l_tot = l_run + wave_shfl_xor(l_run, 32);
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-            const int rloc = 32 * wave + (lane & 31);
+            const int rloc = 32 * rw + (lane & 31);
             const int h = sg.h0 + rloc;
             const int hh = lane >> 5;
             if (final_out) {
@@ -637,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 }
             } else {
                 // blocked partial layout: one 1 KB contiguous store per (d, g) per wave
-                f32x4* wp = (f32x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (wave * 16 * 4) * 64 + lane;
+                f32x4* wp = (f32x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + lane;
                 #pragma unroll
                 for (int d = 0; d < 16; ++d) {
                     #pragma unroll
@@ -648,6 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 }
                 if (hh == 0) p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
             }
+          }
         } else {
             // merge the four waves' states through LDS
             float l_w = l_run + wave_shfl_xor(l_run, 16);
@@ -717,6 +771,10 @@ hipError_t launch_decode(const DecodeParams& p, int variant, bool fp8, bool spar
     if (variant == kV128) {
         if (fp8) return sparse ? launch_one<true, true, kV128>(p, s) : launch_one<true, false, kV128>(p, s);
         return sparse ? launch_one<false, true, kV128>(p, s) : launch_one<false, false, kV128>(p, s);
+    }
+    if (variant == kV64) {
+        if (fp8) return sparse ? launch_one<true, true, kV64>(p, s) : launch_one<true, false, kV64>(p, s);
+        return sparse ? launch_one<false, true, kV64>(p, s) : launch_one<false, false, kV64>(p, s);
     }
     if (fp8) return sparse ? launch_one<true, true, kV16>(p, s) : launch_one<true, false, kV16>(p, s);
     return sparse ? launch_one<false, true, kV16>(p, s) : launch_one<false, false, kV16>(p, s);

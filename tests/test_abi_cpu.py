@@ -30,6 +30,14 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, name), name
 
 
+def test_every_export_declares_argument_types():
+    # without argtypes ctypes passes a Python int as a 32-bit C int, which
+    # truncates device pointers and stream handles
+    L = m.lib()
+    for name in m.EXPORTS:
+        assert getattr(L, name).argtypes is not None, name
+
+
 def test_argument_block_layout_matches_header():
     fields = [f for f, _ in m.MlaDecodeArgs._fields_]
     src = "#include <stdio.h>\n#include <stddef.h>\n#include \"mla.h\"\nint main(void){\n"
@@ -53,8 +61,13 @@ def test_sizes():
     assert m.metadata_size(64, 2, 128, 256) == (256 * 8, 64 * 2 + 1)
     # h_q = 16: row groups of 16
     assert m.metadata_size(16, 1, 16, 256) == (256 * 8, 17)
-    ws = m.workspace_size(16, 1, 128, 256)
+    # 16 < h_q <= 64: 64-head groups
+    assert m.metadata_size(16, 1, 40, 256) == (256 * 8, 16 + 1)
+    ws = m.workspace_size(16, 1, 64, 256)
     slots = 16 + 256
+    assert ws == ((slots * 64 * 512 * 4 + 255) // 256) * 256 + slots * 64 * 4
+    ws = m.workspace_size(64, 1, 128, 256)
+    slots = 64 + 256
     assert ws == ((slots * 128 * 512 * 4 + 255) // 256) * 256 + slots * 128 * 4
 
 
@@ -129,12 +142,12 @@ CASES = [
 def test_decode_argument_errors(over, status, word):
     L = m.lib()
     a = _args(**over)
-    for fn in (L.mla_decode_with_kvcache, L.mla_combine):
+    for fn in (L.mla_decode_with_kvcache, L.mla_decode_splits, L.mla_combine):
         rc = fn(ctypes.byref(a), None)
         msg = L.mla_last_error().decode()
         if fn is L.mla_combine and rc == status:
             assert word in msg
-        if fn is L.mla_decode_with_kvcache:
+        if fn is not L.mla_combine:
             assert rc == status, msg
             assert word in msg, msg
 
@@ -142,6 +155,7 @@ def test_decode_argument_errors(over, status, word):
 def test_null_args_and_metadata_errors():
     L = m.lib()
     assert L.mla_decode_with_kvcache(None, None) == m.MLA_ERR_INVALID
+    assert L.mla_decode_splits(None, None) == m.MLA_ERR_INVALID
     assert L.mla_get_metadata(FAKE, 4, 1, 128, -1, 256, FAKE, FAKE, None) == m.MLA_ERR_INVALID
     assert L.mla_get_metadata(0, 4, 1, 128, 0, 256, FAKE, FAKE, None) == m.MLA_ERR_INVALID
     assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 256, 0, FAKE, None) == m.MLA_ERR_INVALID

@@ -132,3 +132,30 @@ def test_repeat_determinism():
     for _ in range(99):
         again = run_gpu(w, g)
         assert _same(first, again)
+
+
+@pytest.mark.parametrize("fmt,h_q,sparse", [("bf16", 128, False), ("fp8", 16, False), ("fp8", 64, True)])
+def test_split_then_combine_equals_one_call(fmt, h_q, sparse):
+    """mla_decode_splits followed by mla_combine is the same two kernels as
+    mla_decode_with_kvcache: outputs agree bit for bit."""
+    import mla_latent_kv_10_amd as mla
+
+    say(f"splits+combine vs one call {fmt} h_q={h_q} sparse={sparse}")
+    if sparse:
+        w = make_workload(batch=2, s_q=1, h_q=h_q, kv_format=fmt, topk=400, sparse_tokens_per_seq=2048,
+                          invalid_frac=0.05, seed=25)
+    else:
+        w = make_workload(batch=3, s_q=1, h_q=h_q, seqlens=[2000, 1, 900], kv_format=fmt, seed=25)
+    g = to_gpu(w)
+    o1, lse1, tm, so = run_gpu(w, g, num_parts=16)
+    o2 = torch.full_like(o1, float("nan"))
+    lse2 = torch.full_like(lse1, float("nan"))
+    ws = torch.empty((mla.workspace_size(w.batch, w.s_q, w.h_q, 16),), dtype=torch.uint8, device="cuda:0")
+    a = mla.make_args(g["q"], g["kv"], g["block_table"], g["cache_seqlens"], tm, so, w.softmax_scale, w.causal,
+                      fmt == "fp8", g["indices"], ws, o2, lse2)
+    side = torch.cuda.Stream()  # a non-default stream: its handle is a full 64-bit pointer
+    side.wait_stream(torch.cuda.current_stream())
+    mla.mla_decode_splits(a, side.cuda_stream)
+    mla.mla_combine(a, side.cuda_stream)
+    torch.cuda.synchronize()
+    assert _same((o1, lse1), (o2, lse2))

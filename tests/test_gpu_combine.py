@@ -16,13 +16,13 @@ pytestmark = pytest.mark.gpu
 
 def _slot_layout(part_o):
     """Logical partials [S][RG][512] -> the documented workspace layout
-    (RG = 16 row-major; RG = 128 blocked: float4 ((w*16+dd)*4+g)*64+lane holds
-    row 32w+(lane&31), dims 32dd+8g+4(lane>>5)+0..3)."""
+    (RG = 16 row-major; RG = 128 or 64 blocked: float4 ((w*16+dd)*4+g)*64+lane
+    holds row 32w+(lane&31), dims 32dd+8g+4(lane>>5)+0..3)."""
     S, RG, _ = part_o.shape
     if RG == 16:
         return np.ascontiguousarray(part_o)
-    out = np.empty((S, 4, 16, 4, 64, 4), dtype=part_o.dtype)
-    for w in range(4):
+    out = np.empty((S, RG // 32, 16, 4, 64, 4), dtype=part_o.dtype)
+    for w in range(RG // 32):
         for lane in range(64):
             r = 32 * w + (lane & 31)
             h = lane >> 5
@@ -33,12 +33,12 @@ def _slot_layout(part_o):
     return out.reshape(S, RG, 512)
 
 
-@pytest.mark.parametrize("h_q,s_q", [(128, 1), (16, 2), (20, 1)])
-def test_combine_matches_oracle_merge(h_q, s_q):
-    say(f"combine h_q={h_q} s_q={s_q}")
+@pytest.mark.parametrize("h_q,s_q,P", [(128, 1, 8), (64, 1, 64), (16, 2, 8), (20, 1, 8), (100, 2, 8)])
+def test_combine_matches_oracle_merge(h_q, s_q, P):
+    say(f"combine h_q={h_q} s_q={s_q} parts={P}")
     dev = "cuda:0"
-    B, P = 3, 8
-    RG = 16 if h_q <= 64 else 128
+    B = 3
+    RG = 16 if h_q <= 16 else (64 if h_q <= 64 else 128)
     n_hb = -(-h_q // RG)
     n_rg = s_q * n_hb
     Q = B * n_rg

@@ -11,12 +11,15 @@ from tests.gpu_helpers import say
 
 pytestmark = pytest.mark.gpu
 
-# The documented policy (include/mla.h): row groups of 16 heads when h_q <= 64,
-# else 128; (fixed_cost, min_payload) = (1, 1) and (2, 2).
+# The documented policy (include/mla.h): row groups of 16 heads when h_q <= 16,
+# 64 when 16 < h_q <= 64, else 128; (fixed_cost, min_payload) = (1, 1) for 16
+# and (2, 2) for 64 and 128.
 
 
-def _policy(h_q):
-    return (16, 1, 1) if h_q <= 64 else (128, 2, 2)
+def _policy(h_q, s_q, batch, num_parts):
+    if h_q <= 16:
+        return (16, 1, 1)
+    return (64, 2, 2) if h_q <= 64 else (128, 2, 2)
 
 
 CASES = []
@@ -43,7 +46,7 @@ def test_metadata_matches_reference(batch, s_q, h_q, num_parts, topk, seed):
     tm, so = mla.get_mla_metadata(seq if topk == 0 else None, s_q, h_q, topk=topk, num_parts=num_parts,
                                   batch=batch)
     torch.cuda.synchronize()
-    rg, C, Wmin = _policy(h_q)
+    rg, C, Wmin = _policy(h_q, s_q, batch, num_parts)
     T = tile_counts(lens.tolist(), batch, s_q, h_q, topk, rg)
     ref_meta, ref_off = split_schedule(T, num_parts, C, Wmin)
     assert np.array_equal(so.cpu().numpy(), ref_off)

@@ -30,7 +30,11 @@ SMALL = [
     ("bf16 dense h128 ragged", dict(batch=3, s_q=1, h_q=128, seqlens=[1, 130, 700], kv_format="bf16")),
     ("bf16 dense h16 ragged", dict(batch=4, s_q=1, h_q=16, seqlens=[64, 65, 1000, 3], kv_format="bf16")),
     ("bf16 dense h4", dict(batch=2, s_q=1, h_q=4, seqlens=[256, 77], kv_format="bf16")),
-    ("bf16 dense h20 two head blocks", dict(batch=2, s_q=1, h_q=20, seqlens=[300, 129], kv_format="bf16")),
+    ("bf16 dense h20 64-head group", dict(batch=2, s_q=1, h_q=20, seqlens=[300, 129], kv_format="bf16")),
+    ("bf16 dense h64", dict(batch=3, s_q=1, h_q=64, seqlens=[1000, 1, 64], kv_format="bf16")),
+    ("fp8 causal h48 s_q=2", dict(batch=2, s_q=2, h_q=48, seqlens=[700, 33], kv_format="fp8", causal=True)),
+    ("fp8 sparse h64", dict(batch=2, s_q=1, h_q=64, kv_format="fp8", topk=300, sparse_tokens_per_seq=1024,
+                            invalid_frac=0.05)),
     ("bf16 dense h100 padded rows", dict(batch=2, s_q=1, h_q=100, seqlens=[200, 513], kv_format="bf16")),
     ("bf16 dense h130 two row groups", dict(batch=1, s_q=1, h_q=130, seqlens=[333], kv_format="bf16")),
     ("bf16 dense empty sequence", dict(batch=3, s_q=1, h_q=128, seqlens=[0, 100, 0], kv_format="bf16")),
