@@ -54,7 +54,7 @@ def algorithmic_counts(w):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.md")
-KERNEL_SOURCES = ("mla_decode.hip", "mla_common.h", "build.py")
+KERNEL_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_common.h", "build.py")
 
 
 def kernel_source_hash() -> str:

@@ -33,130 +33,12 @@
 #include <type_traits>
 
 #include "mla_common.h"
+#include "mla_device.h"
 
 namespace mla {
 namespace {
 
-#define LDS_AS __attribute__((address_space(3)))
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyMax = 8.0f;  // exponent reference moves when a row max grows by > 2^8
-constexpr unsigned kOOB = 0xFFFFFFFFu;
-
-// ---------------------------------------------------------------- LDS layout
-
-// Byte offset of (token t, 16-byte unit u) inside a swizzled bf16 tile.
-__device__ __forceinline__ int tile_off(int t, int u) {
-    return (((t >> 3) * 9 + (u >> 3)) << 10) + ((((t & 7) << 3) | ((u & 7) ^ ((t >> 1) & 7))) << 4);
-}
-
-template <bool FP8>
-struct Smem {
-    // bf16: two tiles (double buffer). FP8: two raw tiles + one bf16 tile.
-    static constexpr int kTileA = 0;
-    static constexpr int kTileB = FP8 ? -1 : kTileBytes;
-    static constexpr int kRaw0 = FP8 ? kTileBytes : -1;
-    static constexpr int kRaw1 = FP8 ? kTileBytes + kRawTileBytes : -1;
-    static constexpr int kBytes = FP8 ? kTileBytes + 2 * kRawTileBytes : 2 * kTileBytes;
-};
-
-// ---------------------------------------------------------------- waits
-
-__device__ __forceinline__ void wait_vm(int n) {
-    // vmcnt takes an immediate; n is wave-uniform and small.
-    switch (n) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
-        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
-        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-        case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
-        case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
-
-__device__ __forceinline__ void block_sync_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// One 16-byte-per-lane direct load into LDS: lane i's bytes land at dst + 16 i.
-// Global address = base + vindex * stride + voffset + soffset; an out-of-range
-// vindex writes zeros.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char LDS_AS* dst, unsigned vindex, unsigned voffset,
-                                      int soffset) {
-    __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, vindex, voffset, soffset, 0, 0);
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
-
-// bf16x8 from eight floats (round to nearest even).
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
-    bf16x8 r;
-    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
-    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
-    return r;
-}
-
-__device__ __forceinline__ bf16x8 lds_read16(const char LDS_AS* p) { return *(const bf16x8 LDS_AS*)p; }
-
-__device__ __forceinline__ i16x4 lds_read_tr(const char LDS_AS* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p);
-}
-
-
-// acc *= alpha for an accumulator held in AGPRs. Written as inline asm on the
-// AGPRs themselves so the register allocator keeps MFMA accumulators in the
-// AGPR file (a VALU multiply in C++ would make it migrate them to VGPRs). The
-// trailing s_nop covers the VALU-write -> MFMA-srcC hazard; the last MFMA
-// that wrote acc is hundreds of cycles back (a whole QK phase).
-template <typename V, int N>
-__device__ __forceinline__ void scale_agpr(V& acc, float alpha) {
-    #pragma unroll
-    for (int e = 0; e < N; ++e) {
-        float x = acc[e], t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(t) : "v"(alpha));
-        acc[e] = x;
-    }
-}
-
-
-// O += V^T P^T on the AGPR-resident accumulator (v_mfma_f32_32x32x16_bf16).
-// Inline asm pins the accumulator to AGPRs; the rest of the kernel's MFMAs
-// use VGPR accumulators. Hazards around this asm are covered explicitly:
-// callers separate it from VALU producers of its operands and from later
-// AGPR reads with s_nop (mfma_fence).
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// >= 24 wait states: covers XDL-result -> VALU/accvgpr-read and VALU-write -> XDL-read hazards.
-__device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
-// ---------------------------------------------------------------- segment context
-
-struct Seg {
-    int b, i, h0, limit, t_end, split, n_splits, slot, mask_rows;
-};
-
-// Row index of token t of tile k (dense): page base from the block table.
-// Returns kOOB for masked tokens.
-__device__ __forceinline__ unsigned dense_row(int page_row0, int n_valid, int t) {
-    return (page_row0 >= 0 && t < n_valid) ? (unsigned)(page_row0 + t) : kOOB;
-}
+using namespace dev;
 
 // ---------------------------------------------------------------- kernel
 
@@ -222,11 +104,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             unsigned r = kOOB;
             if (k <= t1) {
                 if (SPARSE) {
+                    // raw entry; range-checked where it is used (issue_tile), a
+                    // tile later, so this load is not waited for here
                     const int pos = k * kBlock + lane;
-                    if (pos < p.topk) {
-                        const int v = idx_row[pos];
-                        r = (v >= 0 && v < p.num_rows) ? (unsigned)v : kOOB;
-                    }
+                    if (pos < p.topk) r = (unsigned)idx_row[pos];
                 } else {
                     r = (unsigned)p.block_table[(int64_t)sg.b * p.mbps + k];
                 }
@@ -250,6 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 n_valid = min(kBlock, sg.limit - k * kBlock);
                 mask = (page0 < 0 || n_valid <= 0) ? 0ull : (n_valid >= 64 ? ~0ull : ((1ull << n_valid) - 1ull));
             } else {
+                srow = ((int)srow >= 0 && (int)srow < p.num_rows) ? srow : kOOB;  // -1 and out of range
                 mask = __builtin_amdgcn_ballot_w64(srow != kOOB);
             }
             if (!FP8) {

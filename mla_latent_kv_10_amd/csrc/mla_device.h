@@ -1,0 +1,230 @@
+// Device helpers shared by the split-decode kernels (gfx950 only).
+#pragma once
+
+#include <type_traits>
+
+#include "mla_common.h"
+
+namespace mla {
+namespace dev {
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;  // exponent reference moves when a row max grows by > 2^8
+constexpr unsigned kOOB = 0xFFFFFFFFu;
+
+// ---------------------------------------------------------------- LDS layout
+
+// Byte offset of (token t, 16-byte unit u) inside a swizzled bf16 tile.
+__device__ __forceinline__ int tile_off(int t, int u) {
+    return (((t >> 3) * 9 + (u >> 3)) << 10) + ((((t & 7) << 3) | ((u & 7) ^ ((t >> 1) & 7))) << 4);
+}
+
+template <bool FP8>
+struct Smem {
+    // bf16: two tiles (double buffer). FP8: two raw tiles + one bf16 tile.
+    static constexpr int kTileA = 0;
+    static constexpr int kTileB = FP8 ? -1 : kTileBytes;
+    static constexpr int kRaw0 = FP8 ? kTileBytes : -1;
+    static constexpr int kRaw1 = FP8 ? kTileBytes + kRawTileBytes : -1;
+    static constexpr int kBytes = FP8 ? kTileBytes + 2 * kRawTileBytes : 2 * kTileBytes;
+};
+
+// ---------------------------------------------------------------- waits
+
+__device__ __forceinline__ void wait_vm(int n) {
+    // vmcnt takes an immediate; n is wave-uniform. Counts past the table wait for everything.
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+        case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+        case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+        case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
+        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+        case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
+        case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+        case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+        case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+        case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
+        case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+        case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
+        case 26: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
+        case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+        case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+        case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
+        case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+        case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+__device__ __forceinline__ void wait_lgkm(int n) {
+    // lgkmcnt takes a 4-bit immediate; n is a compile-time constant after unrolling.
+    switch (n) {
+        case 0: asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt lgkmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt lgkmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt lgkmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt lgkmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt lgkmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt lgkmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt lgkmcnt(14)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt lgkmcnt(15)" ::: "memory"); break;
+    }
+}
+
+// ---------------------------------------------------------------- opaque LDS-direct loads
+// Buffer descriptor words (gfx9 V#): base, stride, record count, and a
+// 32-bit data format so bounds checking applies to every access.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int stride, unsigned num_records) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = (unsigned)a;
+    r[1] = ((unsigned)(a >> 32) & 0xFFFFu) | ((unsigned)stride << 16);
+    r[2] = num_records;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// buffer_load_dwordx4 ... lds issued as inline asm: lane i's 16 bytes land at
+// LDS address lds + 16 i; global address = base + vindex * stride + voffset;
+// an out-of-range vindex writes zeros. The compiler does not see this as a
+// memory operation, so it neither counts it in vmcnt nor waits for it before
+// LDS reads it cannot prove disjoint; callers wait with wait_vm and order LDS
+// reuse with workgroup barriers. Nothing is written to registers.
+// lds and rsrc must be wave-uniform; they are moved to SGPRs here.
+__device__ __forceinline__ u32x4 sgpr4(const u32x4& r) {
+    u32x4 o;
+    o[0] = __builtin_amdgcn_readfirstlane(r[0]);
+    o[1] = __builtin_amdgcn_readfirstlane(r[1]);
+    o[2] = __builtin_amdgcn_readfirstlane(r[2]);
+    o[3] = __builtin_amdgcn_readfirstlane(r[3]);
+    return o;
+}
+
+__device__ __forceinline__ void dma16_opaque(const u32x4& rsrc, unsigned lds, unsigned vindex, unsigned voffset) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    const u32x2 va = {vindex, voffset};
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(sgpr4(rsrc)) : "m0");
+}
+
+// buffer_load_dword ... lds (raw buffer, byte offset per lane): lane i's
+// 4 bytes land at lds + 4 i. Same visibility rules as dma16_opaque.
+__device__ __forceinline__ void dma4_opaque(const u32x4& rsrc, unsigned lds, unsigned voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(sgpr4(rsrc)) : "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void LDS_AS* p) { return (unsigned)(uintptr_t)p; }
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+__device__ __forceinline__ void block_sync_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane direct load into LDS: lane i's bytes land at dst + 16 i.
+// Global address = base + vindex * stride + voffset + soffset; an out-of-range
+// vindex writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char LDS_AS* dst, unsigned vindex, unsigned voffset,
+                                      int soffset) {
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, vindex, voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// bf16x8 from eight floats (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const char LDS_AS* p) { return *(const bf16x8 LDS_AS*)p; }
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char LDS_AS* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p);
+}
+
+
+// acc *= alpha for an accumulator held in AGPRs. Written as inline asm on the
+// AGPRs themselves so the register allocator keeps MFMA accumulators in the
+// AGPR file (a VALU multiply in C++ would make it migrate them to VGPRs). The
+// trailing s_nop covers the VALU-write -> MFMA-srcC hazard; the last MFMA
+// that wrote acc is hundreds of cycles back (a whole QK phase).
+template <typename V, int N>
+__device__ __forceinline__ void scale_agpr(V& acc, float alpha) {
+    #pragma unroll
+    for (int e = 0; e < N; ++e) {
+        float x = acc[e], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t) : "v"(alpha));
+        acc[e] = x;
+    }
+}
+
+
+// O += V^T P^T on the AGPR-resident accumulator (v_mfma_f32_32x32x16_bf16).
+// Inline asm pins the accumulator to AGPRs; the rest of the kernel's MFMAs
+// use VGPR accumulators. Hazards around this asm are covered explicitly:
+// callers separate it from VALU producers of its operands and from later
+// AGPR reads with s_nop (mfma_fence).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// >= 24 wait states: covers XDL-result -> VALU/accvgpr-read and VALU-write -> XDL-read hazards.
+__device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// ---------------------------------------------------------------- segment context
+
+struct Seg {
+    int b, i, h0, limit, t_end, split, n_splits, slot, mask_rows;
+};
+
+// Row index of token t of tile k (dense): page base from the block table.
+// Returns kOOB for masked tokens.
+__device__ __forceinline__ unsigned dense_row(int page_row0, int n_valid, int t) {
+    return (page_row0 >= 0 && t < n_valid) ? (unsigned)(page_row0 + t) : kOOB;
+}
+
+}  // namespace dev
+}  // namespace mla
