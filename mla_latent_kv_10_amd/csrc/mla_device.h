@@ -1,8 +1,6 @@
 // Device helpers shared by the split-decode kernels (gfx950 only).
 #pragma once
 
-#include <type_traits>
-
 #include "mla_common.h"
 
 namespace mla {
@@ -77,81 +75,6 @@ __device__ __forceinline__ void wait_vm(int n) {
         case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
         case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
-
-__device__ __forceinline__ void wait_lgkm(int n) {
-    // lgkmcnt takes a 4-bit immediate; n is a compile-time constant after unrolling.
-    switch (n) {
-        case 0: asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory"); break;
-        case 4: asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory"); break;
-        case 5: asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory"); break;
-        case 6: asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory"); break;
-        case 7: asm volatile("s_waitcnt lgkmcnt(7)" ::: "memory"); break;
-        case 8: asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory"); break;
-        case 9: asm volatile("s_waitcnt lgkmcnt(9)" ::: "memory"); break;
-        case 10: asm volatile("s_waitcnt lgkmcnt(10)" ::: "memory"); break;
-        case 11: asm volatile("s_waitcnt lgkmcnt(11)" ::: "memory"); break;
-        case 12: asm volatile("s_waitcnt lgkmcnt(12)" ::: "memory"); break;
-        case 13: asm volatile("s_waitcnt lgkmcnt(13)" ::: "memory"); break;
-        case 14: asm volatile("s_waitcnt lgkmcnt(14)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt lgkmcnt(15)" ::: "memory"); break;
-    }
-}
-
-// ---------------------------------------------------------------- opaque LDS-direct loads
-// Buffer descriptor words (gfx9 V#): base, stride, record count, and a
-// 32-bit data format so bounds checking applies to every access.
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, int stride, unsigned num_records) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    u32x4 r;
-    r[0] = (unsigned)a;
-    r[1] = ((unsigned)(a >> 32) & 0xFFFFu) | ((unsigned)stride << 16);
-    r[2] = num_records;
-    r[3] = 0x00020000u;
-    return r;
-}
-
-// buffer_load_dwordx4 ... lds issued as inline asm: lane i's 16 bytes land at
-// LDS address lds + 16 i; global address = base + vindex * stride + voffset;
-// an out-of-range vindex writes zeros. The compiler does not see this as a
-// memory operation, so it neither counts it in vmcnt nor waits for it before
-// LDS reads it cannot prove disjoint; callers wait with wait_vm and order LDS
-// reuse with workgroup barriers. Nothing is written to registers.
-// lds and rsrc must be wave-uniform; they are moved to SGPRs here.
-__device__ __forceinline__ u32x4 sgpr4(const u32x4& r) {
-    u32x4 o;
-    o[0] = __builtin_amdgcn_readfirstlane(r[0]);
-    o[1] = __builtin_amdgcn_readfirstlane(r[1]);
-    o[2] = __builtin_amdgcn_readfirstlane(r[2]);
-    o[3] = __builtin_amdgcn_readfirstlane(r[3]);
-    return o;
-}
-
-__device__ __forceinline__ void dma16_opaque(const u32x4& rsrc, unsigned lds, unsigned vindex, unsigned voffset) {
-    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-    const u32x2 va = {vindex, voffset};
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(sgpr4(rsrc)) : "m0");
-}
-
-// buffer_load_dword ... lds (raw buffer, byte offset per lane): lane i's
-// 4 bytes land at lds + 4 i. Same visibility rules as dma16_opaque.
-__device__ __forceinline__ void dma4_opaque(const u32x4& rsrc, unsigned lds, unsigned voffset) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(sgpr4(rsrc)) : "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const void LDS_AS* p) { return (unsigned)(uintptr_t)p; }
-
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
     }
 }
 
