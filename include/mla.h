@@ -62,8 +62,14 @@ extern "C" {
  *   or ceil(topk / 64) tiles (sparse). Units are laid end to end, each
  *   non-empty one first taking FIXED_COST positions, then one per tile; with
  *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
- *   MIN_PAYLOAD), the tile at position x goes to part floor(x / W).
- *   FIXED_COST and MIN_PAYLOAD: RG 128 or 64 -> 2 and 2; RG 16 -> 1 and 1.
+ *   MIN_PAYLOAD), the tile at position x goes to work part floor(x / W).
+ *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 4; RG 64 -> 2 and 2;
+ *   RG 16 -> 1 and 1.
+ *   Placement: when num_parts is a multiple of 8, with used = ceil(total / W)
+ *   and k = ceil(used / 8), work part j is row (j / k) * (num_parts / 8) +
+ *   j % k of tile_meta and every other row is empty (the decode grid runs
+ *   row r on XCD r / (num_parts / 8), so the parts with work are spread over
+ *   the eight XCDs); otherwise work part j is row j.
  */
 
 /* Message for the last non-OK status on this thread ("" if none). */
@@ -99,9 +105,9 @@ int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes
  *   cache_seqlens  device int32 [batch]; ignored when topk > 0 (may be NULL)
  *   topk           0 for dense attention, else the sparse index count
  *   num_parts      parts (workgroups) of the decode grid, 1..65535
- *   tile_meta      device int32 [num_parts][8], 16-byte aligned, written: per part
- *                  {q_begin, t_begin, q_end, t_end (inclusive), first_split,
- *                   empty, 0, 0}
+ *   tile_meta      device int32 [num_parts][8], 16-byte aligned, written: per row
+ *                  (placed as above) {q_begin, t_begin, q_end, t_end
+ *                  (inclusive), first_split, empty, 0, 0}
  *   split_offsets  device int32 [Q + 1], written: prefix sums of the number
  *                  of splits of each row-group sequence
  * The result is a pure function of (cache_seqlens, batch, s_q, h_q, topk,

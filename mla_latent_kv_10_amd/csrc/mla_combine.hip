@@ -26,17 +26,17 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 template <int RG>
 struct CombineMap {
     // blocks per row-group sequence, float4s per thread per slot
-    static constexpr int kBlocksPerQ = RG == 16 ? 4 : RG / 8;  // 128 -> 16, 64 -> 8
-    static constexpr int kVec = RG == 16 ? 2 : 4;
+    static constexpr int kBlocksPerQ = RG == 16 ? 4 : RG / 4;  // 128 -> 32, 64 -> 16
+    static constexpr int kVec = 2;
     // thread -> (row, float4 offsets within the slot, dims of each float4)
     __device__ static void map(int blk, int t, int& row, int (&f4)[kVec], int (&dim)[kVec]) {
         if constexpr (RG != 16) {
-            const int w = blk >> 2, dq = blk & 3;
+            const int w = blk >> 3, dq = blk & 7;
             const int lane = t & 63, g = (t >> 6) & 3;
             row = 32 * w + (lane & 31);
             #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const int dd = 4 * dq + j;
+                const int dd = 2 * dq + j;
                 f4[j] = ((w * 16 + dd) * 4 + g) * 64 + lane;
                 dim[j] = 32 * dd + 8 * g + 4 * (lane >> 5);
             }
@@ -53,11 +53,20 @@ struct CombineMap {
     }
 };
 
+// One pass over the splits, kU at a time: every load of a chunk (its lse
+// values and its partial rows) is issued before any of them is used, and the
+// running reference m moves with a rescale of the sums, as in the online
+// softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} o_k / s with
+// s = sum_k e^{lse_k - m}, lse = m + ln s.
 template <int RG>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     using M = CombineMap<RG>;
-    const int q = blockIdx.x / M::kBlocksPerQ;
-    const int blk = blockIdx.x - q * M::kBlocksPerQ;
+    // XCD-aware numbering, as in the split kernel: the parts of one sequence
+    // run on one XCD, so its partials are merged on the XCD that wrote them.
+    int lb = blockIdx.x;
+    if ((gridDim.x & 7) == 0) lb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int q = lb / M::kBlocksPerQ;
+    const int blk = lb - q * M::kBlocksPerQ;
     const int b = q / p.n_rg;
     const int rgi = q - b * p.n_rg;
     const int i = rgi / p.n_hb;
@@ -72,62 +81,52 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     uint16_t* op = p.o + orow * kDv;
     const float* lse_k = p.ws_lse + (int64_t)s0 * RG + row;
     const bool lse_writer = dim[0] == 0;  // exactly one thread per row holds dim 0
-    // max and sum of e^{lse_k - max} over the splits, 16 independent loads at a time
-    constexpr int kB = 16;
-    float m = -INFINITY;
-    for (int k0 = 0; k0 < n; k0 += kB) {
-        float lv[kB];
-        #pragma unroll
-        for (int u = 0; u < kB; ++u) lv[u] = (k0 + u < n) ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
-        #pragma unroll
-        for (int u = 0; u < kB; ++u) m = fmaxf(m, lv[u]);
-    }
-    if (n == 0 || m == -INFINITY) {
-        #pragma unroll
-        for (int j = 0; j < M::kVec; ++j) *(i16x4*)(op + dim[j]) = i16x4{};
-        if (lse_writer) p.lse[orow] = -INFINITY;
-        return;
-    }
-    float s = 0.f;
-    for (int k0 = 0; k0 < n; k0 += kB) {
-        float lv[kB];
-        #pragma unroll
-        for (int u = 0; u < kB; ++u) lv[u] = (k0 + u < n) ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
-        #pragma unroll
-        for (int u = 0; u < kB; ++u) s += lv[u] == -INFINITY ? 0.f : __expf(lv[u] - m);
-    }
-    const float lse = m + __logf(s);
+    const f32x4* base = (const f32x4*)(p.ws_o + (int64_t)s0 * RG * kDv);
+    constexpr int kSlot4 = RG * kDv / 4;  // float4s per slot
+    constexpr int kU = 16;                // splits in flight
+    float m = -INFINITY, s = 0.f;
     f32x4 acc[M::kVec];
     #pragma unroll
     for (int j = 0; j < M::kVec; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4* base = (const f32x4*)(p.ws_o + (int64_t)s0 * RG * kDv);
-    constexpr int kSlot4 = RG * kDv / 4;  // float4s per slot
-    constexpr int kU = 8;                 // splits in flight
     for (int k0 = 0; k0 < n; k0 += kU) {
-        float wgt[kU];
+        float lv[kU];
         f32x4 v[kU][M::kVec];
         #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const bool in = k0 + u < n;
-            const float lk = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
-            wgt[u] = lk == -INFINITY ? 0.f : __expf(lk - lse);
+            lv[u] = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
             #pragma unroll
             for (int j = 0; j < M::kVec; ++j)
                 v[u][j] = in ? base[(int64_t)(k0 + u) * kSlot4 + f4[j]] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        float mc = m;
         #pragma unroll
-        for (int u = 0; u < kU; ++u)
+        for (int u = 0; u < kU; ++u) mc = fmaxf(mc, lv[u]);
+        if (mc == -INFINITY) continue;  // nothing attended so far
+        const float r = (m == -INFINITY) ? 0.f : __expf(m - mc);
+        s *= r;
+        #pragma unroll
+        for (int j = 0; j < M::kVec; ++j) acc[j] *= r;
+        #pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const float wgt = lv[u] == -INFINITY ? 0.f : __expf(lv[u] - mc);
+            s += wgt;
             #pragma unroll
-            for (int j = 0; j < M::kVec; ++j) acc[j] += wgt[u] * v[u][j];
+            for (int j = 0; j < M::kVec; ++j) acc[j] += wgt * v[u][j];
+        }
+        m = mc;
     }
+    // no split attended anything (or no split at all): o = 0, lse = -inf
+    const bool empty = m == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / s;
     #pragma unroll
     for (int j = 0; j < M::kVec; ++j) {
         i16x4 o4;
         #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(short, (__bf16)acc[j][e]);
+        for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(short, (__bf16)(acc[j][e] * inv));
         *(i16x4*)(op + dim[j]) = o4;
     }
-    if (lse_writer) p.lse[orow] = lse;
+    if (lse_writer) p.lse[orow] = empty ? -INFINITY : m + __logf(s);
 }
 
 }  // namespace

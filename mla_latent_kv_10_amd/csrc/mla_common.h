@@ -46,7 +46,7 @@ inline Layout layout_for(int h_q, int s_q, int batch, int num_parts) {
     } else if (h_q <= 64) {
         l.rg = 64; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV64;
     } else {
-        l.rg = 128; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV128;
+        l.rg = 128; l.fixed_cost = 2; l.min_payload = 4; l.variant = kV128;
     }
     l.n_hb = (h_q + l.rg - 1) / l.rg;
     l.n_rg = s_q * l.n_hb;

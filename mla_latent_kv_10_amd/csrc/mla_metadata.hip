@@ -4,10 +4,12 @@
 // decide which row-group sequences and which 64-token tiles each part (one
 // workgroup of the decode grid) processes, and how many splits each
 // sequence has; every layer reuses the result. The rule (see include/mla.h):
-// units laid end to end, fixed_cost positions then one per tile, part =
-// floor(position / W). One workgroup of 1024 threads computes it: block-wide
-// exclusive scans built from wave shuffles (positions, last non-empty unit,
-// split counts), then a binary search per part.
+// units laid end to end, fixed_cost positions then one per tile, work part
+// floor(position / W); then the work parts are placed on the grid so that the
+// ones holding work are spread evenly over the eight XCDs. One workgroup of
+// 1024 threads computes it: block-wide exclusive scans built from wave
+// shuffles (positions, last non-empty unit, split counts), then a binary
+// search per part.
 #include "mla_common.h"
 
 namespace mla {
@@ -129,12 +131,26 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
     }
     __syncthreads();  // s_cum / s_prev complete before the searches
 
-    for (int part = tid; part < p.num_parts; part += kMT) {
-        int32_t* out = p.tile_meta + (int64_t)part * 8;
+    // Placement. The decode grid runs row r of tile_meta on XCD r / (P / 8)
+    // when P % 8 == 0, so work part j goes to row (j / k) * (P / 8) + j % k,
+    // k = ceil(used / 8): every XCD gets k consecutive work parts (adjacent
+    // parts share a sequence, hence its q in that XCD's L2), and the rows
+    // past them stay empty. Otherwise row r holds work part r.
+    const int used = total > 0 ? (int)((total + W - 1) / W) : 0;  // work parts that may hold tiles
+    const int per_xcd = p.num_parts >> 3;
+    const bool spread = (p.num_parts & 7) == 0;
+    const int kx = (used + 7) >> 3;
+    for (int r = tid; r < p.num_parts; r += kMT) {
+        int32_t* out = p.tile_meta + (int64_t)r * 8;
+        int part = r;
+        if (spread) {
+            const int x = r / per_xcd, c = r - x * per_xcd;
+            part = c < kx ? x * kx + c : p.num_parts;  // num_parts: no work part
+        }
         const long long start = (long long)part * W;
         const long long end = start + W - 1;  // inclusive
         int row[8] = {0, 0, 0, 0, 0, 1, 0, 0};
-        if (Q > 0 && start < total) {
+        if (Q > 0 && part < p.num_parts && start < total) {
             const int qb = first_unit_past(s_cum, Q, (int)start);
             const int x0b = s_cum[qb] + C;
             const int tb = (int)max(0LL, start - x0b);

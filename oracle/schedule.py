@@ -18,6 +18,12 @@ assignment (the GPU computes the same result per part, in parallel):
     W = max(ceil(total / num_parts), min_payload), the tile at position x
     belongs to part floor(x / W).
   * A unit's splits are the distinct parts among its tiles, in order.
+  * Placement on the grid: with used = ceil(total / W) work parts that can
+    hold tiles and num_parts a multiple of 8, work part j is written to row
+    (j // k) * (num_parts // 8) + j % k of tile_meta, k = ceil(used / 8);
+    every other row is empty. (The decode grid runs row r on XCD
+    r // (num_parts // 8), so the parts holding work are spread over all
+    eight XCDs, k consecutive ones each.) Otherwise work part j is row j.
 """
 
 from __future__ import annotations
@@ -71,13 +77,21 @@ def split_schedule(T: Sequence[int], num_parts: int, fixed_cost: int, min_payloa
             n_splits[q] = len({owner[(q, t)] for t in range(t_count)})
     split_offsets = np.zeros(len(T) + 1, dtype=np.int32)
     split_offsets[1:] = np.cumsum(n_splits)
+    used = -(-total // W) if total > 0 else 0
+    row_of = list(range(num_parts))
+    if num_parts % 8 == 0:
+        per_xcd = num_parts // 8
+        k = -(-used // 8)
+        row_of = [None] * num_parts
+        for j in range(used):
+            row_of[j] = (j // k) * per_xcd + j % k
     meta = np.zeros((num_parts, 8), dtype=np.int32)
+    meta[:, 5] = 1
     for p, tiles in enumerate(parts):
         if not tiles:
-            meta[p, 5] = 1
             continue
         qb, tb = tiles[0]
         qe, te = tiles[-1]
         first_split = len({owner[(qb, t)] for t in range(tb)})
-        meta[p, :6] = [qb, tb, qe, te, first_split, 0]
+        meta[row_of[p], :6] = [qb, tb, qe, te, first_split, 0]
     return meta, split_offsets

@@ -72,3 +72,26 @@ def test_tile_counts_layout():
     assert tile_counts([130], 1, 1, 20, 0, 16) == [3, 3]
     # sparse ignores cache_seqlens
     assert tile_counts([5, 5], 2, 1, 128, 2048, 128) == [32, 32]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_placement_spreads_work_over_xcds(seed):
+    # num_parts a multiple of 8: the rows holding work lie in the first k rows
+    # of each of the eight row blocks (one block per XCD); a work part that
+    # holds only fixed-cost positions, or lies past the last tile, is empty
+    rng = np.random.default_rng(100 + seed)
+    Q = int(rng.integers(1, 30))
+    T = [int(x) for x in rng.integers(0, 40, Q)]
+    P = int(rng.choice([8, 16, 64, 256]))
+    C, Wmin = int(rng.integers(0, 4)), int(rng.integers(1, 9))
+    meta, _ = split_schedule(T, P, C, Wmin)
+    total = sum(C + t for t in T if t > 0)
+    W = max(-(-total // P) if total else 1, Wmin)
+    used = -(-total // W) if total else 0
+    k = -(-used // 8)
+    per = P // 8
+    busy = meta[:, 5] == 0
+    for x in range(8):
+        blk = busy[x * per:(x + 1) * per]
+        assert not blk[k:].any()
+    assert int(busy.sum()) <= used
