@@ -72,40 +72,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         const int rgi = qq - sg.b * p.n_rg;
         sg.i = rgi / p.n_hb;
         sg.h0 = (rgi - sg.i * p.n_hb) * RG;
-        int T_q;
-        if (SPARSE) {
-            T_q = (p.topk + kBlock - 1) / kBlock;
-            sg.limit = p.topk;
-        } else {
-            const int L = uniform(p.seqlens[sg.b]);
-            T_q = L > 0 ? (L + kBlock - 1) / kBlock : 0;
-            int lim = p.causal ? L - p.s_q + 1 + sg.i : L;
-            lim = min(lim, min(L, p.mbps * kBlock));
-            sg.limit = max(lim, 0);
-        }
         const int t0 = (qq == qb) ? tb : 0;
-        int t1 = (qq == qe) ? te : T_q - 1;
-        sg.split = (qq == qb) ? fs : 0;
-        const int so = uniform(p.split_offsets[qq]);
-        sg.n_splits = uniform(p.split_offsets[qq + 1]) - so;
-        sg.slot = so + sg.split;
-        const int t_eff = (sg.limit + kBlock - 1) / kBlock;  // tiles holding any attended token
-        t1 = min(t1, t_eff - 1);
-        sg.t_end = t1;
-
-        // ------------------------------------------------ per-segment state
         const int64_t qrow0 = ((int64_t)sg.b * p.s_q + sg.i) * p.h_q;  // row index of head 0
         const int32_t* idx_row = SPARSE ? p.indices + ((int64_t)sg.b * p.s_q + sg.i) * p.topk : nullptr;
 
-        // Per-tile index prefetch, three tiles ahead of use, as one VMEM load per
-        // wave: sparse -> lane l holds the cache row of token l (kOOB when
-        // masked); dense -> every lane holds the tile's page id.
-        auto fetch_index = [&](int k) -> unsigned {
+        // Index word of tile k, one VMEM load per wave: sparse -> lane l holds
+        // the raw index entry of token l (range-checked where the tile is
+        // issued); dense -> every lane holds the tile's page id. `kmax` bounds
+        // the block-table read; words past the segment's last tile are never used.
+        auto load_index = [&](int k, int kmax) -> unsigned {
             unsigned r = kOOB;
-            if (k <= t1) {
+            if (k <= kmax) {
                 if (SPARSE) {
-                    // raw entry; range-checked where it is used (issue_tile), a
-                    // tile later, so this load is not waited for here
                     const int pos = k * kBlock + lane;
                     if (pos < p.topk) r = (unsigned)idx_row[pos];
                 } else {
@@ -114,6 +92,60 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             return r;
         };
+
+        // Everything that gates the first tile goes out as one batch before any
+        // of it is used: the index words of tiles t0..t0+2 (bounded by the
+        // block-table row, so they need not wait for the sequence length), the
+        // length and split offsets, then q. The first tile's load is issued as
+        // soon as its index word arrives, while q is still in flight.
+        const int kmax0 = SPARSE ? (p.topk + kBlock - 1) / kBlock - 1 : p.mbps - 1;
+        unsigned idx_a = load_index(t0, kmax0), idx_b = load_index(t0 + 1, kmax0), idx_c = load_index(t0 + 2, kmax0);
+        const int len_raw = SPARSE ? 0 : p.seqlens[sg.b];
+        const int so_raw = p.split_offsets[qq], so_end_raw = p.split_offsets[qq + 1];
+
+        constexpr bool R32 = VAR != kV16;               // 32 rows per wave, 32x32x16 MFMA
+        constexpr int NQ = R32 ? 36 : 18;   // k-steps over 576 dims
+        bf16x8 qreg[NQ];
+        {
+            const int ln = opaque(lane);
+            int row, dsub;
+            if constexpr (R32) { row = 32 * ((VAR == kV64) ? (wave >> 1) : wave) + (ln & 31); dsub = 8 * (ln >> 5); }
+            else { row = ln & 15; dsub = 8 * (ln >> 4); }
+            // Rows past h_q (padding of the last row group) load head 0's q:
+            // rows are independent and a padded row's output is never stored.
+            const int h = sg.h0 + row;
+            const uint16_t* qbase = p.q + qrow0 * kDqk;           // head 0 of this query position
+            const int qoff = (h < p.h_q ? h : 0) * kDqk + dsub;   // this lane's row and sub-block
+            #pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) {
+                const int dim0 = R32 ? 16 * kk : 32 * kk;
+                qreg[kk] = __builtin_bit_cast(bf16x8, *(const i16x8*)(qbase + qoff + dim0));
+            }
+        }
+
+        int T_q;
+        if (SPARSE) {
+            T_q = (p.topk + kBlock - 1) / kBlock;
+            sg.limit = p.topk;
+        } else {
+            const int L = uniform(len_raw);
+            T_q = L > 0 ? (L + kBlock - 1) / kBlock : 0;
+            int lim = p.causal ? L - p.s_q + 1 + sg.i : L;
+            lim = min(lim, min(L, p.mbps * kBlock));
+            sg.limit = max(lim, 0);
+        }
+        int t1 = (qq == qe) ? te : T_q - 1;
+        sg.split = (qq == qb) ? fs : 0;
+        const int so = uniform(so_raw);
+        sg.n_splits = uniform(so_end_raw) - so;
+        sg.slot = so + sg.split;
+        const int t_eff = (sg.limit + kBlock - 1) / kBlock;  // tiles holding any attended token
+        t1 = min(t1, t_eff - 1);
+        sg.t_end = t1;
+
+        // ------------------------------------------------ per-segment state
+        // Index words of later tiles (three tiles ahead of use).
+        auto fetch_index = [&](int k) -> unsigned { return load_index(k, t1); };
         // Dense: row of token 0 of tile k, or -1 when the page id is invalid.
         auto dense_page_row0 = [&](unsigned blk_bits) -> int {
             const int blk = uniform((int)blk_bits);
@@ -123,7 +155,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // Issue the DMA of tile k into LDS region `dst`; returns the tile's
         // validity mask (bit t set = token t attended). The number of VMEM
         // instructions per wave is fixed per variant (n_dma).
-        auto issue_tile = [&](int k, char LDS_AS* dst, unsigned srow) -> uint64_t {
+        // UNROLL: straight-line issue (the prologue), so the compiler's own
+        // wait counts for loads issued before it (q) are exact.
+        auto issue_tile = [&](auto unroll_tag, int k, char LDS_AS* dst, unsigned srow) -> uint64_t {
+            constexpr bool UNROLL = decltype(unroll_tag)::value;
             int page0 = 0, n_valid = 0;
             uint64_t mask;
             if (!SPARSE) {
@@ -136,30 +171,51 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             if (!FP8) {
                 // 72 chunks, 18 per wave: token groups 2w, 2w+1; unit groups 0..8.
-                #pragma unroll 1
-                for (int g = 0; g < 2; ++g) {
+                auto group = [&](int g) {
+                    // lane geometry recomputed here (not hoisted and spilled: a
+                    // scratch reload would make the issue wait for q)
+                    const int ln = opaque(lane);
                     const int tg = 2 * wave + g;
-                    const int t = tg * 8 + (lane >> 3);
-                    const int uu = (lane & 7) ^ ((t >> 1) & 7);
+                    const int t = tg * 8 + (ln >> 3);
+                    const int uu = (ln & 7) ^ ((t >> 1) & 7);
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
                     else row = dense_row(page0, n_valid, t);
-                    #pragma unroll 1
-                    for (int ug = 0; ug < 9; ++ug) {
-                        dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                    if constexpr (UNROLL) {
+                        #pragma unroll
+                        for (int ug = 0; ug < 9; ++ug)
+                            dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                    } else {
+                        #pragma unroll 1
+                        for (int ug = 0; ug < 9; ++ug)
+                            dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
                     }
+                };
+                if constexpr (UNROLL) {
+                    group(0);
+                    group(1);
+                } else {
+                    #pragma unroll 1
+                    for (int g = 0; g < 2; ++g) group(g);
                 }
             } else {
                 // 41 chunks of the raw tile image, chunk c to wave c % 4.
-                #pragma unroll 1
-                for (int c = wave; c < kRawUnits; c += 4) {
-                    const int kk = c * 64 + lane;
+                auto chunk = [&](int c) {
+                    const int kk = c * 64 + opaque(lane);
                     const int t = (kk * 1599) >> 16;  // kk / 41, exact for kk < 2624
                     const int u = kk - t * kRawUnits;
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
                     else row = dense_row(page0, n_valid, t);
                     dma16(kv_rsrc, dst + (c << 10), row, (unsigned)(u << 4), 0);
+                };
+                if constexpr (UNROLL) {
+                    #pragma unroll
+                    for (int j = 0; j < 10; ++j) chunk(wave + 4 * j);
+                    if (wave == 0) chunk(40);
+                } else {
+                    #pragma unroll 1
+                    for (int c = wave; c < kRawUnits; c += 4) chunk(c);
                 }
             }
             return mask;
@@ -209,35 +265,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // V64 : wave owns rows 32*rw + (lane & 31) and tokens 32*tw .. +31 of
         //       each tile (rw = wave >> 1, tw = wave & 1).
         // V16 : wave owns tokens 16*wave .. +15 of each tile; all 16 rows.
-        constexpr bool R32 = VAR != kV16;               // 32 rows per wave, 32x32x16 MFMA
         constexpr int NB = (VAR == kV128) ? 2 : 1;      // 32-token blocks per wave per tile
         const int rw = (VAR == kV64) ? (wave >> 1) : wave;
         const int tw = (VAR == kV64) ? (wave & 1) : 0;
-        constexpr int NQ = R32 ? 36 : 18;   // k-steps over 576 dims
         constexpr int NO = R32 ? 16 : 32;   // output blocks over 512 dims
-        bf16x8 qreg[NQ];
         typedef typename std::conditional<R32, f32x16, f32x4>::type Acc;
         Acc oacc[NO];
         #pragma unroll
         for (int d = 0; d < NO; ++d) oacc[d] = Acc{};
         float m_run = -INFINITY;  // exponent reference (log2 units), per row
         float l_run = 0.f;        // partial sum of p over this lane's tokens
-
-        {
-            int row, dsub;
-            if constexpr (R32) { row = 32 * rw + (lane & 31); dsub = 8 * (lane >> 5); }
-            else { row = lane & 15; dsub = 8 * (lane >> 4); }
-            const int h = sg.h0 + row;
-            const bool ok = h < p.h_q;
-            const uint16_t* qp = p.q + (qrow0 + (ok ? h : 0)) * kDqk + dsub;
-            #pragma unroll
-            for (int kk = 0; kk < NQ; ++kk) {
-                const int dim0 = R32 ? 16 * kk : 32 * kk;
-                i16x8 v = *(const i16x8*)(qp + dim0);
-                if (!ok) v = i16x8{};
-                qreg[kk] = __builtin_bit_cast(bf16x8, v);
-            }
-        }
 
         // Per-lane LDS offsets (see the layout derivation in the comments).
         int koff[2][4];   // 32-row variants: [token block][k-step & 3]; V16 uses koff[0][0..1]
@@ -476,10 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             char LDS_AS* stage0 = smem + (FP8 ? S::kRaw0 : S::kTileA);
             char LDS_AS* stage1 = smem + (FP8 ? S::kRaw1 : S::kTileB);
             char LDS_AS* ctile = smem + S::kTileA;  // FP8: the single bf16 tile
-            // index prefetch ring: tiles k, k+1, k+2
-            unsigned idx_a = fetch_index(t0), idx_b = fetch_index(t0 + 1), idx_c = fetch_index(t0 + 2);
-            uint64_t mask_a = issue_tile(t0, stage0, idx_a), mask_b = 0;
-            if (t0 + 1 <= t1) mask_b = issue_tile(t0 + 1, stage1, idx_b);
+            // index prefetch ring: tiles k, k+1, k+2 (loaded above)
+            constexpr std::true_type kUnrolled{};
+            constexpr std::false_type kLooped{};
+            uint64_t mask_a = issue_tile(kUnrolled, t0, stage0, idx_a), mask_b = 0;
+            if (t0 + 1 <= t1) mask_b = issue_tile(kUnrolled, t0 + 1, stage1, idx_b);
+            // q was loaded before these tiles: have it in registers here, with the
+            // tiles still in flight, so no wait for it lands inside the tile loop.
+            #pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) asm volatile("" ::"v"(qreg[kk]));
             for (int k = t0; k <= t1; ++k) {
                 const bool odd = ((k - t0) & 1) != 0;
                 char LDS_AS* cur = odd ? stage1 : stage0;
@@ -498,12 +540,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if (FP8) {
                     dequant(cur, ctile);
                     block_sync_lds();
-                    if (k + 2 <= t1) mask_c = issue_tile(k + 2, cur, idx_c);
+                    if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                     compute_tile(ctile, mask_a);
                 } else {
                     compute_tile(cur, mask_a);
                     block_sync_lds();
-                    if (k + 2 <= t1) mask_c = issue_tile(k + 2, cur, idx_c);
+                    if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                 }
                 idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
                 mask_a = mask_b; mask_b = mask_c;

@@ -92,6 +92,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char LDS_AS* dst
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The value unchanged, but opaque to the optimiser: lane-dependent addresses
+// computed from it inside a loop are not hoisted out of the loop (and then
+// spilled to scratch across it).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // bf16x8 from eight floats (round to nearest even).
