@@ -7,16 +7,16 @@
 // units laid end to end, fixed_cost positions then one per tile, work part
 // floor(position / W); then the work parts are placed on the grid so that the
 // ones holding work are spread evenly over the eight XCDs. One workgroup of
-// 1024 threads computes it: block-wide exclusive scans built from wave
-// shuffles (positions, last non-empty unit, split counts), then a binary
-// search per part.
+// 256 threads computes it: block-wide exclusive scans built from wave
+// shuffles (positions with the last non-empty unit in one pass, then split
+// counts), then a binary search per part.
 #include "mla_common.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kMT = 1024;
+constexpr int kMT = 256;
 constexpr int kWaves = kMT / 64;
 
 enum ScanOp { kSum, kMax };
@@ -55,6 +55,37 @@ __device__ int block_exclusive_scan(int v, int identity, int* scratch, int* tota
     return combine<OP>(before, exc);
 }
 
+// Exclusive scans of two values per thread at once, a sum and a max, with one
+// set of barriers. Returns (sum before, max before); *sum_total receives the
+// sum over all threads.
+__device__ int2 block_exclusive_scan_sum_max(int vs, int vm, int2* scratch, int* sum_total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int is = vs, im = vm;
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int us = __shfl_up(is, off, 64), um = __shfl_up(im, off, 64);
+        if (lane >= off) { is += us; im = max(im, um); }
+    }
+    int es = __shfl_up(is, 1, 64), em = __shfl_up(im, 1, 64);
+    if (lane == 0) { es = 0; em = -1; }
+    if (lane == 63) scratch[w] = make_int2(is, im);
+    __syncthreads();
+    if (w == 0) {
+        int2 v = lane < kWaves ? scratch[lane] : make_int2(0, -1);
+        #pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int us = __shfl_up(v.x, off, 64), um = __shfl_up(v.y, off, 64);
+            if (lane >= off) { v.x += us; v.y = max(v.y, um); }
+        }
+        if (lane < kWaves) scratch[lane] = v;  // inclusive over waves
+    }
+    __syncthreads();
+    const int2 before = w > 0 ? scratch[w - 1] : make_int2(0, -1);
+    *sum_total = scratch[kWaves - 1].x;
+    __syncthreads();
+    return make_int2(before.x + es, max(before.y, em));
+}
+
 // Smallest q in [0, n) with cum[q + 1] > v (cum has n + 1 entries, non-decreasing).
 __device__ int first_unit_past(const int* cum, int n, int v) {
     int lo = 0, hi = n - 1;
@@ -70,10 +101,11 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
     __shared__ int s_T[kMaxUnits];          // tiles per unit
     __shared__ int s_prev[kMaxUnits];       // last non-empty unit at or before q (-1 if none)
     __shared__ int s_scan[kWaves];
+    __shared__ int2 s_scan2[kWaves];
     const int Q = p.batch * p.n_rg;
     const int tid = threadIdx.x;
     const int C = p.fixed_cost;
-    const int per = (Q + kMT - 1) / kMT;    // <= 8 units per thread
+    const int per = (Q + kMT - 1) / kMT;    // <= 32 units per thread
     const int b0 = tid * per, e0 = min(Q, b0 + per);
 
     // tiles and cost of this thread's (contiguous) units
@@ -90,9 +122,9 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
         cost_sum += T > 0 ? C + T : 0;
         if (T > 0) last_ne = q;
     }
-    int total, unused;
-    const int cost_before = block_exclusive_scan<kSum>(cost_sum, 0, s_scan, &total);
-    const int ne_before = block_exclusive_scan<kMax>(last_ne, -1, s_scan, &unused);
+    int total;
+    const int2 before = block_exclusive_scan_sum_max(cost_sum, last_ne, s_scan2, &total);
+    const int cost_before = before.x, ne_before = before.y;
     {
         int run = cost_before, prev = ne_before;
         for (int q = b0; q < e0; ++q) {
