@@ -42,7 +42,7 @@ inline Layout layout_for(int h_q, int s_q, int batch, int num_parts) {
     (void)num_parts;
     Layout l;
     if (h_q <= 16) {
-        l.rg = 16; l.fixed_cost = 1; l.min_payload = 1; l.variant = kV16;
+        l.rg = 16; l.fixed_cost = 0; l.min_payload = 1; l.variant = kV16;
     } else if (h_q <= 64) {
         l.rg = 64; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV64;
     } else {
