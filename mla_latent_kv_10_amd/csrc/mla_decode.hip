@@ -45,7 +45,20 @@ using namespace dev;
 template <bool FP8, bool SPARSE, int VAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     using S = Smem<FP8>;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[S::kBytes];
+    // FP8 with 128-head groups spreads each tile's loads over the PV MFMAs of
+    // the tile two ahead (see the tile pipeline). Its bf16 tile and its two raw
+    // tiles are separate LDS arrays, so the compiler can tell the loads in
+    // flight from the operand reads and waits only where a buffer is reused;
+    // each raw array has a spare 1 KB after the tile for the padding load of
+    // waves 1..3 (41 chunks over 4 waves). The other variants share one array
+    // (the 64- and 16-head ones reuse all of it for their end-of-segment merge).
+    constexpr bool kPvLoads = FP8 && VAR == kV128;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kPvLoads ? 1024 : S::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_tile[kPvLoads ? kTileBytes : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw0[kPvLoads ? kRawTileBytes + 1024 : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw1[kPvLoads ? kRawTileBytes + 1024 : 1024];
+    // sparse index words of four tiles (tile x in slot x & 3), 64 per tile
+    __shared__ __attribute__((aligned(256))) int32_t lds_ring[kPvLoads && SPARSE ? 4 * 64 : 1];
     char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -86,6 +99,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if (SPARSE) {
                     const int pos = k * kBlock + lane;
                     if (pos < p.topk) r = (unsigned)idx_row[pos];
+                } else if constexpr (kPvLoads) {
+                    // read-only for the whole kernel: a scalar load (lgkmcnt),
+                    // outside the vmcnt count that tracks the tile loads
+                    typedef const int32_t __attribute__((address_space(4))) cint32;
+                    r = (unsigned)((cint32*)p.block_table)[(int64_t)sg.b * p.mbps + k];
                 } else {
                     r = (unsigned)p.block_table[(int64_t)sg.b * p.mbps + k];
                 }
@@ -99,7 +117,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // length and split offsets, then q. The first tile's load is issued as
         // soon as its index word arrives, while q is still in flight.
         const int kmax0 = SPARSE ? (p.topk + kBlock - 1) / kBlock - 1 : p.mbps - 1;
-        unsigned idx_a = load_index(t0, kmax0), idx_b = load_index(t0 + 1, kmax0), idx_c = load_index(t0 + 2, kmax0);
+        // Sparse, FP8, 128-head groups: the index words travel to the LDS ring
+        // (every wave loads the whole slot and reads only what it loaded), so
+        // no register carries a pending load across tile-loop iterations.
+        const u32x4 ix_words = make_rsrc_words(p.indices, 0, (unsigned)(p.batch * p.s_q * p.topk) * 4u);
+        const int ix_row0 = ((sg.b * p.s_q + sg.i) * p.topk);
+        auto ring_load = [&](int k) {
+            dma4_asm(ix_words, lds_addr((const char LDS_AS*)(lds_ring + (k & 3) * 64)),
+                     (unsigned)(ix_row0 + k * kBlock + (opaque(lane) & 63)) * 4u);
+        };
+        unsigned idx_a = kOOB, idx_b = kOOB, idx_c = kOOB;
+        if constexpr (kPvLoads && SPARSE) {
+            ring_load(t0);
+            ring_load(t0 + 1);
+            ring_load(t0 + 2);
+        } else {
+            idx_a = load_index(t0, kmax0);
+            idx_b = load_index(t0 + 1, kmax0);
+            idx_c = load_index(t0 + 2, kmax0);
+        }
         const int len_raw = SPARSE ? 0 : p.seqlens[sg.b];
         const int so_raw = p.split_offsets[qq], so_end_raw = p.split_offsets[qq + 1];
 
@@ -157,18 +193,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // instructions per wave is fixed per variant (n_dma).
         // UNROLL: straight-line issue (the prologue), so the compiler's own
         // wait counts for loads issued before it (q) are exact.
-        auto issue_tile = [&](auto unroll_tag, int k, char LDS_AS* dst, unsigned srow) -> uint64_t {
-            constexpr bool UNROLL = decltype(unroll_tag)::value;
-            int page0 = 0, n_valid = 0;
+        // Where tile k's rows come from, given its index word: dense -> the
+        // page's first cache row and the attended token count; sparse -> each
+        // lane's (token's) validated cache row. mask: bit t set = token t attended.
+        struct TileSrc {
+            int page0, n_valid;
+            unsigned srow;
             uint64_t mask;
+        };
+        auto tile_src = [&](int k, unsigned word) -> TileSrc {
+            TileSrc ts{0, 0, kOOB, 0ull};
             if (!SPARSE) {
-                page0 = dense_page_row0(srow);
-                n_valid = min(kBlock, sg.limit - k * kBlock);
-                mask = (page0 < 0 || n_valid <= 0) ? 0ull : (n_valid >= 64 ? ~0ull : ((1ull << n_valid) - 1ull));
+                ts.page0 = dense_page_row0(word);
+                ts.n_valid = min(kBlock, sg.limit - k * kBlock);
+                ts.mask = (ts.page0 < 0 || ts.n_valid <= 0) ? 0ull
+                          : (ts.n_valid >= 64 ? ~0ull : ((1ull << ts.n_valid) - 1ull));
             } else {
-                srow = ((int)srow >= 0 && (int)srow < p.num_rows) ? srow : kOOB;  // -1 and out of range
-                mask = __builtin_amdgcn_ballot_w64(srow != kOOB);
+                const bool in_row = k * kBlock + lane < p.topk;  // ring words past topk belong to other rows
+                ts.srow = (in_row && (int)word >= 0 && (int)word < p.num_rows) ? word : kOOB;  // -1, out of range
+                ts.mask = __builtin_amdgcn_ballot_w64(ts.srow != kOOB);
             }
+            return ts;
+        };
+        auto issue_tile = [&](auto unroll_tag, int k, char LDS_AS* dst, unsigned word) -> uint64_t {
+            constexpr bool UNROLL = decltype(unroll_tag)::value;
+            const TileSrc ts = tile_src(k, word);
+            const int page0 = ts.page0, n_valid = ts.n_valid;
+            const unsigned srow = ts.srow;
+            const uint64_t mask = ts.mask;
             if (!FP8) {
                 // 72 chunks, 18 per wave: token groups 2w, 2w+1; unit groups 0..8.
                 auto group = [&](int g) {
@@ -200,14 +252,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 }
             } else {
                 // 41 chunks of the raw tile image, chunk c to wave c % 4.
+                // Chunk c holds 16-byte units kk = 64 c + lane of the image:
+                // token kk / 41, unit kk % 41. From chunk c to c + 4, kk grows by
+                // 256 = 6 * 41 + 10, so (token, unit) step without a division.
+                const int kk0 = 64 * wave + opaque(lane);
+                int t = (kk0 * 1599) >> 16;  // kk0 / 41, exact for kk0 < 2624
+                int u = kk0 - t * kRawUnits;
                 auto chunk = [&](int c) {
-                    const int kk = c * 64 + opaque(lane);
-                    const int t = (kk * 1599) >> 16;  // kk / 41, exact for kk < 2624
-                    const int u = kk - t * kRawUnits;
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
                     else row = dense_row(page0, n_valid, t);
                     dma16(kv_rsrc, dst + (c << 10), row, (unsigned)(u << 4), 0);
+                    u += 10;
+                    t += 6;
+                    if (u >= kRawUnits) { u -= kRawUnits; t += 1; }
                 };
                 if constexpr (UNROLL) {
                     #pragma unroll
@@ -220,7 +278,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             return mask;
         };
-        const int n_dma = FP8 ? (wave == 0 ? 11 : 10) : 18;
+        const int n_dma = kPvLoads ? 11 : (FP8 ? (wave == 0 ? 11 : 10) : 18);
+
+        // FP8, 128-head groups: chunk j (0..10) of a tile's raw image; chunk
+        // c = wave + 4 j holds 16-byte units kk = 64 c + lane (token kk / 41,
+        // unit kk % 41). Branch-free, so it can sit between MFMAs: waves 1..3
+        // have no chunk 10 and load nothing into the spare 1 KB after the tile
+        // instead, and a tile past the segment (no rows) loads nothing.
+        const u32x4 kv_words = make_rsrc_words(p.kv, p.row_bytes, (unsigned)p.num_rows);
+        struct ChunkAddr {
+            unsigned row, voff;
+        };
+        auto chunk_addr = [&](int j, const TileSrc& ts) -> ChunkAddr {
+            const int c = wave + 4 * j;
+            const int kk = 64 * c + (opaque(lane) & 63);
+            const int t = (int)(__umul24((unsigned)kk, 1599u) >> 16);  // kk / 41, exact for kk < 2624
+            const int u = kk - (int)__umul24((unsigned)t, (unsigned)kRawUnits);
+            unsigned row;
+            if (SPARSE) {
+                // the chunk's 64 units span tokens tA .. tA + 2
+                const int tA = uniform((64 * c * 1599) >> 16);
+                const unsigned rA = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA, 63));
+                const unsigned rB = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA + 1, 63));
+                const unsigned rC = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA + 2, 63));
+                row = t == tA ? rA : (t == tA + 1 ? rB : rC);
+            } else {
+                row = dense_row(ts.page0, ts.n_valid, t);
+            }
+            return ChunkAddr{c < kRawUnits ? row : kOOB, (unsigned)(u << 4)};
+        };
+        auto chunk_issue = [&](int j, char LDS_AS* dst, const ChunkAddr& a) {
+            const int c = wave + 4 * j;
+            dma16_asm(kv_words, lds_addr(dst + ((c < kRawUnits ? c : kRawUnits) << 10)), a.row, a.voff);
+        };
+        auto raw_chunk = [&](int j, char LDS_AS* dst, const TileSrc& ts) { chunk_issue(j, dst, chunk_addr(j, ts)); };
 
         // Dequantise raw FP8 tile `raw` into the bf16 tile at `tile`. Lane l
         // handles token l; wave w handles raw latent units w, w+4, .., w+28
@@ -317,7 +408,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
 
         // ------------------------------------------------ compute one tile
-        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask) {
+        // side(j), j = 0..10, runs after PV MFMA 6 j when kSide (the next-but-one
+        // tile's loads; see the tile pipeline).
+        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto side_tag, auto&& side) {
+            constexpr bool kSide = decltype(side_tag)::value;
             if constexpr (R32) {
                 // S^T = K Q^T on 32x32x16 MFMAs: two accumulation chains (the two
                 // token blocks for V128; even/odd k-steps of the one block for V64).
@@ -422,11 +516,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int j = 0; j < kVF; ++j) va[j] = vread(j);
                 mfma_fence();  // pb (VALU) -> MFMA operand
+                constexpr int kSideEvery = 6, kSideN = 11;
                 #pragma unroll
                 for (int n = 0; n < NPV; ++n) {
                     if (n + kVF < NPV) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
                     const int cl = n >> 4, d = n & 15;
                     mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[cl]);
+                    if constexpr (kSide) {
+                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN) side(n / kSideEvery);
+                    }
                 }
                 mfma_fence();  // MFMA results -> later AGPR reads / scaling
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVF, 0);
@@ -434,6 +532,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 for (int n = 0; n < NPV - kVF; ++n) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    if constexpr (kSide) {
+                        // a load every kSideEvery MFMAs, its address VALU two per
+                        // MFMA in the slots before it
+                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN)
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        else
+                            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                    }
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, kVF, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -509,7 +615,74 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         };
 
         // ------------------------------------------------ tile pipeline
-        if (t0 <= t1) {
+        if constexpr (kPvLoads) {
+          if (t0 <= t1) {
+            // Tile k: wait for its raw image, dequantise it into the bf16 tile,
+            // then compute it while tile k + 2's loads (into the raw buffer just
+            // dequantised) go out between its PV MFMAs, one every 6 MFMAs: a CU
+            // takes an LDS-direct load every ~25 cycles, so loads issued back to
+            // back stall the issuing waves, but spread this way they do not.
+            // The loop is unrolled by two so that each raw buffer has a fixed
+            // role in each half.
+            char LDS_AS* tile = (char LDS_AS*)lds_tile;
+            char LDS_AS* raw0 = (char LDS_AS*)lds_raw0;
+            char LDS_AS* raw1 = (char LDS_AS*)lds_raw1;
+            const TileSrc none{-1, 0, kOOB, 0ull};
+            // index word of tile k (sparse: from the ring, its load complete)
+            auto word_of = [&](int k, unsigned reg) -> unsigned {
+                if constexpr (SPARSE) return (unsigned)lds_ring[(k & 3) * 64 + lane];
+                else return reg;
+            };
+            if constexpr (SPARSE) wait_vm(36);  // the ring loads of t0..t0+2 (older than the split offsets and the 36 q loads)
+            TileSrc ts = tile_src(t0, word_of(t0, idx_a));
+            uint64_t mask_a = ts.mask, mask_b = 0;
+            #pragma unroll
+            for (int j = 0; j < 11; ++j) raw_chunk(j, raw0, ts);
+            if (t0 + 1 <= t1) {
+                ts = tile_src(t0 + 1, word_of(t0 + 1, idx_b));
+                mask_b = ts.mask;
+                #pragma unroll
+                for (int j = 0; j < 11; ++j) raw_chunk(j, raw1, ts);
+            }
+            // q was loaded before these tiles: have it in registers here. (The
+            // compiler does not see the tile loads, so its wait for q also
+            // waits for them: once per segment.)
+            #pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) asm volatile("" ::"v"(qreg[kk]));
+            for (int k = t0; k <= t1; ++k) {
+                char LDS_AS* cur = ((k - t0) & 1) ? raw1 : raw0;
+                unsigned idx_d = kOOB;
+                if constexpr (SPARSE) ring_load(k + 3);  // always issued: a fixed count per iteration
+                else idx_d = fetch_index(k + 3);
+                // VMEM instructions issued after tile k's loads: tile k + 1's
+                // (11; in the prologue only if that tile exists), and for the
+                // sparse index the ring loads of tiles k + 2 and k + 3 (dense
+                // index words are scalar loads).
+                int after;
+                if (k == t0) after = (k + 1 <= t1 ? 11 : 0) + (SPARSE ? 1 : 0);
+                else after = 11 + (SPARSE ? 2 : 0);
+                wait_vm(after);
+                block_sync_lds();
+                dequant(cur, tile);
+                block_sync_lds();
+                // sparse: the ring load of tile k + 2 (followed by tile k + 1's
+                // loads and the ring load of k + 3); at k = t0 it is already in
+                if (SPARSE && k > t0) wait_vm(12);
+                const TileSrc tn = (k + 2 <= t1) ? tile_src(k + 2, word_of(k + 2, idx_c)) : none;
+                // chunk j is issued with the address computed after chunk j - 1,
+                // so its VALU fills the MFMA slots between the two loads
+                ChunkAddr ca = chunk_addr(0, tn);
+                compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
+                    chunk_issue(j, cur, ca);
+                    if (j + 1 < 11) ca = chunk_addr(j + 1, tn);
+                });
+                idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
+                mask_a = mask_b; mask_b = tn.mask;
+            }
+            wait_vm(0);        // the loads for tiles past the segment have landed
+            block_sync_lds();  // every wave is done with the tiles before LDS is reused
+          }
+        } else if (t0 <= t1) {
             char LDS_AS* stage0 = smem + (FP8 ? S::kRaw0 : S::kTileA);
             char LDS_AS* stage1 = smem + (FP8 ? S::kRaw1 : S::kTileB);
             char LDS_AS* ctile = smem + S::kTileA;  // FP8: the single bf16 tile
@@ -541,9 +714,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     dequant(cur, ctile);
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
-                    compute_tile(ctile, mask_a);
+                    compute_tile(ctile, mask_a, std::false_type{}, [](int) {});
                 } else {
-                    compute_tile(cur, mask_a);
+                    compute_tile(cur, mask_a, std::false_type{}, [](int) {});
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                 }

@@ -92,6 +92,54 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char LDS_AS* dst
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Buffer descriptor words (gfx9 V#): base, stride, record count, and a 32-bit
+// data format so that the bounds check applies to every access; the same
+// descriptor as __builtin_amdgcn_make_buffer_rsrc(base, stride, records, 0x20000).
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, int stride, unsigned num_records) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = (unsigned)a;
+    r[1] = ((unsigned)(a >> 32) & 0xFFFFu) | ((unsigned)stride << 16);
+    r[2] = num_records;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One 4-byte-per-lane direct load into LDS as inline asm, raw buffer with a
+// byte offset per lane (lane i's word lands at lds + 4 i; an offset past the
+// record count reads 0). Same rules as dma16_asm below.
+__device__ __forceinline__ void dma4_asm(const u32x4& rsrc, unsigned lds, unsigned voffset) {
+    u32x4 rs;
+    rs[0] = __builtin_amdgcn_readfirstlane(rsrc[0]);
+    rs[1] = __builtin_amdgcn_readfirstlane(rsrc[1]);
+    rs[2] = __builtin_amdgcn_readfirstlane(rsrc[2]);
+    rs[3] = __builtin_amdgcn_readfirstlane(rsrc[3]);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rs) : "m0");
+}
+
+// LDS byte address of an LDS pointer (what M0 takes).
+__device__ __forceinline__ unsigned lds_addr(const char LDS_AS* p) { return (unsigned)(uintptr_t)p; }
+
+// One 16-byte-per-lane direct load into LDS as inline asm (lane i's bytes land
+// at LDS address lds + 16 i; global address = base + vindex * stride +
+// voffset; an out-of-range vindex writes zeros). The compiler does not see a
+// memory operation here: it neither counts it in its own vmcnt bookkeeping nor
+// waits for it before LDS reads it cannot prove disjoint. Callers wait with
+// wait_vm (the hardware counter does count it) and order LDS reuse with
+// workgroup barriers. lds and rsrc must be wave-uniform.
+__device__ __forceinline__ void dma16_asm(const u32x4& rsrc, unsigned lds, unsigned vindex, unsigned voffset) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    const u32x2 va = {vindex, voffset};
+    u32x4 rs;
+    rs[0] = __builtin_amdgcn_readfirstlane(rsrc[0]);
+    rs[1] = __builtin_amdgcn_readfirstlane(rsrc[1]);
+    rs[2] = __builtin_amdgcn_readfirstlane(rsrc[2]);
+    rs[3] = __builtin_amdgcn_readfirstlane(rsrc[3]);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(rs) : "m0");
+}
+
 // The value unchanged, but opaque to the optimiser: lane-dependent addresses
 // computed from it inside a loop are not hoisted out of the loop (and then
 // spilled to scratch across it).
