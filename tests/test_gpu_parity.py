@@ -47,6 +47,11 @@ SMALL = [
                              invalid_frac=0.05)),
     ("fp8 sparse h16 s_q=2", dict(batch=2, s_q=2, h_q=16, kv_format="fp8", topk=130, sparse_tokens_per_seq=512,
                                   invalid_frac=0.1)),
+    # FP8 with 128 heads: short segments (tile loads past a segment's end,
+    # parts that span several sequences) and the sparse index ring
+    ("fp8 dense h128 short sequences", dict(batch=6, s_q=1, h_q=128, seqlens=[1, 65, 129, 2, 64, 300], kv_format="fp8")),
+    ("fp8 sparse h128 s_q=2", dict(batch=3, s_q=2, h_q=128, kv_format="fp8", topk=130, sparse_tokens_per_seq=704,
+                                   invalid_frac=0.1)),
     ("bf16 sparse h128", dict(batch=2, s_q=1, h_q=128, kv_format="bf16", topk=256, sparse_tokens_per_seq=2048,
                               invalid_frac=0.05)),
     ("bf16 sparse h4 mostly invalid", dict(batch=2, s_q=1, h_q=4, kv_format="bf16", topk=100,
