@@ -53,6 +53,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // waves 1..3 (41 chunks over 4 waves). The other variants share one array
     // (the 64- and 16-head ones reuse all of it for their end-of-segment merge).
     constexpr bool kPvLoads = FP8 && VAR == kV128;
+    // Dense bf16 with 128-head groups issues each tile's loads between the
+    // score MFMAs of the tile before it (see the tile pipeline).
+    constexpr bool kQkLoads = !FP8 && !SPARSE && VAR == kV128;
+    // Both read dense block-table words as scalar loads.
+    constexpr bool kScalarIdx = (kPvLoads || kQkLoads) && !SPARSE;
     __shared__ __attribute__((aligned(1024))) char smem_raw[kPvLoads ? 1024 : S::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_tile[kPvLoads ? kTileBytes : 1024];
     __shared__ __attribute__((aligned(1024))) char lds_raw0[kPvLoads ? kRawTileBytes + 1024 : 1024];
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if (SPARSE) {
                     const int pos = k * kBlock + lane;
                     if (pos < p.topk) r = (unsigned)idx_row[pos];
-                } else if constexpr (kPvLoads) {
+                } else if constexpr (kScalarIdx) {
                     // read-only for the whole kernel: a scalar load (lgkmcnt),
                     // outside the vmcnt count that tracks the tile loads
                     typedef const int32_t __attribute__((address_space(4))) cint32;
@@ -408,10 +413,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
 
         // ------------------------------------------------ compute one tile
-        // side(j), j = 0..10, runs after PV MFMA 6 j when kSide (the next-but-one
-        // tile's loads; see the tile pipeline).
-        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto side_tag, auto&& side) {
-            constexpr bool kSide = decltype(side_tag)::value;
+        // Side work between MFMAs (tile loads; see the tile pipeline):
+        //   side(0, j), j = 0..17, after the score MFMAs of k-step 2 j (j < 17)
+        //     or 33 (j = 17), when the first tag is true;
+        //   side(1, j), j = 0..10, after PV MFMA 6 j, when the second tag is true.
+        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto qk_tag, auto pv_tag, auto&& side) {
+            constexpr bool kSideQk = decltype(qk_tag)::value;
+            constexpr bool kSide = decltype(pv_tag)::value;
             if constexpr (R32) {
                 // S^T = K Q^T on 32x32x16 MFMAs: two accumulation chains (the two
                 // token blocks for V128; even/odd k-steps of the one block for V64).
@@ -435,6 +443,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                         const int ch = (NB == 2) ? bb : (kk & 1);
                         sc[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][bb], qreg[kk], sc[ch], 0, 0, 0);
                     }
+                    if constexpr (kSideQk) {
+                        if (kk < 33 && kk % 2 == 0) side(0, kk / 2);
+                        else if (kk == 33) side(0, 17);
+                    }
                 }
                 // keep the read-ahead: reads first, then (NB MFMA, NB reads) groups
                 __builtin_amdgcn_sched_group_barrier(0x100, NB * kPF, 0);
@@ -442,6 +454,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 for (int kk = 0; kk < 36 - kPF; ++kk) {
                     __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
+                    if constexpr (kSideQk) {
+                        if ((kk < 33 && kk % 2 == 0) || kk == 33) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NB * kPF, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     const int cl = n >> 4, d = n & 15;
                     mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[cl]);
                     if constexpr (kSide) {
-                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN) side(n / kSideEvery);
+                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN) side(1, n / kSideEvery);
                     }
                 }
                 mfma_fence();  // MFMA results -> later AGPR reads / scaling
@@ -672,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // chunk j is issued with the address computed after chunk j - 1,
                 // so its VALU fills the MFMA slots between the two loads
                 ChunkAddr ca = chunk_addr(0, tn);
-                compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
+                compute_tile(tile, mask_a, std::false_type{}, std::true_type{}, [&](int, int j) {
                     chunk_issue(j, cur, ca);
                     if (j + 1 < 11) ca = chunk_addr(j + 1, tn);
                 });
@@ -680,6 +695,60 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 mask_a = mask_b; mask_b = tn.mask;
             }
             wait_vm(0);        // the loads for tiles past the segment have landed
+            block_sync_lds();  // every wave is done with the tiles before LDS is reused
+          }
+        } else if constexpr (kQkLoads) {
+          if (t0 <= t1) {
+            // Tile k + 1's loads go out between tile k's score MFMAs (one per
+            // two k-steps per wave, ~one per 32 cycles per CU) into the other
+            // buffer, which held tile k - 1 (every wave is past it at the
+            // barrier). Issued back to back after the tile they block the waves
+            // for ~1800 cycles (a CU accepts an LDS-direct load every ~25).
+            char LDS_AS* buf0 = smem + S::kTileA;
+            char LDS_AS* buf1 = smem + S::kTileB;
+            const TileSrc none{-1, 0, kOOB, 0ull};
+            // lane geometry of this wave's chunks: token groups tg = 2w + g
+            const int ln = opaque(lane) & 63;
+            int trow[2], uu16[2];
+            #pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int t = (2 * wave + g) * 8 + (ln >> 3);
+                trow[g] = t;
+                uu16[g] = ((ln & 7) ^ ((t >> 1) & 7)) << 4;
+            }
+            // chunk j of a tile: token group g = j / 9, unit group ug = j % 9
+            auto qk_chunk = [&](int j, char LDS_AS* dst, const unsigned (&rows)[2]) {
+                const int g = j / 9, ug = j % 9;
+                dma16_asm(kv_words, lds_addr(dst + (((2 * wave + g) * 9 + ug) << 10)), rows[g], (unsigned)uu16[g], ug * 128);
+            };
+            auto tile_rows = [&](const TileSrc& tsrc, unsigned (&rows)[2]) {
+                #pragma unroll
+                for (int g = 0; g < 2; ++g) rows[g] = dense_row(tsrc.page0, tsrc.n_valid, trow[g]);
+            };
+            TileSrc ts = tile_src(t0, idx_a);
+            uint64_t mask_a = ts.mask;
+            unsigned rows0[2];
+            tile_rows(ts, rows0);
+            #pragma unroll
+            for (int j = 0; j < 18; ++j) qk_chunk(j, buf0, rows0);
+            // q was loaded before the tile: have it in registers here.
+            #pragma unroll
+            for (int kk = 0; kk < NQ; ++kk) asm volatile("" ::"v"(qreg[kk]));
+            unsigned idx_n = idx_b;  // index word of tile k + 1
+            for (int k = t0; k <= t1; ++k) {
+                char LDS_AS* cur = ((k - t0) & 1) ? buf1 : buf0;
+                char LDS_AS* nxt = ((k - t0) & 1) ? buf0 : buf1;
+                const unsigned idx_f = fetch_index(k + 2);
+                wait_vm(0);        // tile k's loads are the only VMEM in flight
+                block_sync_lds();  // ... and every wave is done with nxt (tile k - 1)
+                const TileSrc tn = (k + 1 <= t1) ? tile_src(k + 1, idx_n) : none;
+                unsigned rows[2];
+                tile_rows(tn, rows);
+                compute_tile(cur, mask_a, std::true_type{}, std::false_type{}, [&](int, int j) { qk_chunk(j, nxt, rows); });
+                mask_a = tn.mask;
+                idx_n = idx_f;
+            }
+            wait_vm(0);        // the loads for a tile past the segment have landed
             block_sync_lds();  // every wave is done with the tiles before LDS is reused
           }
         } else if (t0 <= t1) {
@@ -714,9 +783,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     dequant(cur, ctile);
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
-                    compute_tile(ctile, mask_a, std::false_type{}, [](int) {});
+                    compute_tile(ctile, mask_a, std::false_type{}, std::false_type{}, [](int, int) {});
                 } else {
-                    compute_tile(cur, mask_a, std::false_type{}, [](int) {});
+                    compute_tile(cur, mask_a, std::false_type{}, std::false_type{}, [](int, int) {});
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                 }

@@ -128,14 +128,16 @@ __device__ __forceinline__ unsigned lds_addr(const char LDS_AS* p) { return (uns
 
 // One 16-byte-per-lane direct load into LDS as inline asm, non-temporal like
 // dma16 (lane i's bytes land at LDS address lds + 16 i; global address =
-// base + vindex * stride + voffset; an out-of-range vindex writes zeros). The compiler does not see a
+// base + vindex * stride + voffset + soffset; an out-of-range vindex writes
+// zeros). The compiler does not see a
 // memory operation here: it neither counts it in its own vmcnt bookkeeping nor
 // waits for it before LDS reads it cannot prove disjoint. Callers wait with
 // wait_vm (the hardware counter does count it) and order LDS reuse with
 // workgroup barriers. lds and rsrc must be wave-uniform. M0 (the LDS base of
 // the load) is saved and restored around it: the compiler does not honour an
 // M0 clobber, so the asm leaves M0 as it found it.
-__device__ __forceinline__ void dma16_asm(const u32x4& rsrc, unsigned lds, unsigned vindex, unsigned voffset) {
+__device__ __forceinline__ void dma16_asm(const u32x4& rsrc, unsigned lds, unsigned vindex, unsigned voffset,
+                                          int soffset = 0) {
     typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
     const u32x2 va = {vindex, voffset};
     u32x4 rs;
@@ -144,9 +146,10 @@ __device__ __forceinline__ void dma16_asm(const u32x4& rsrc, unsigned lds, unsig
     rs[2] = __builtin_amdgcn_readfirstlane(rsrc[2]);
     rs[3] = __builtin_amdgcn_readfirstlane(rsrc[3]);
     unsigned saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 idxen offen nt lds\n\t"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 idxen offen nt lds\n\t"
                  "s_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(rs));
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soffset)));
 }
 
 // The value unchanged, but opaque to the optimiser: lane-dependent addresses
