@@ -45,25 +45,25 @@ using namespace dev;
 template <bool FP8, bool SPARSE, int VAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     using S = Smem<FP8>;
-    // FP8 with 128-head groups spreads each tile's loads over the PV MFMAs of
-    // the tile two ahead (see the tile pipeline). Its bf16 tile and its two raw
+    // FP8 with 128-head groups spreads each tile's loads over the score MFMAs
+    // of the tile two ahead (see the tile pipeline). Its bf16 tile and its two raw
     // tiles are separate LDS arrays, so the compiler can tell the loads in
     // flight from the operand reads and waits only where a buffer is reused;
     // each raw array has a spare 1 KB after the tile for the padding load of
     // waves 1..3 (41 chunks over 4 waves). The other variants share one array
     // (the 64- and 16-head ones reuse all of it for their end-of-segment merge).
-    constexpr bool kPvLoads = FP8 && VAR == kV128;
+    constexpr bool kFp8Pipe = FP8 && VAR == kV128;
     // Dense bf16 with 128-head groups issues each tile's loads between the
     // score MFMAs of the tile before it (see the tile pipeline).
     constexpr bool kQkLoads = !FP8 && !SPARSE && VAR == kV128;
     // Both read dense block-table words as scalar loads.
-    constexpr bool kScalarIdx = (kPvLoads || kQkLoads) && !SPARSE;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kPvLoads ? 1024 : S::kBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_tile[kPvLoads ? kTileBytes : 1024];
-    __shared__ __attribute__((aligned(1024))) char lds_raw0[kPvLoads ? kRawTileBytes + 1024 : 1024];
-    __shared__ __attribute__((aligned(1024))) char lds_raw1[kPvLoads ? kRawTileBytes + 1024 : 1024];
+    constexpr bool kScalarIdx = (kFp8Pipe || kQkLoads) && !SPARSE;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8Pipe ? 1024 : S::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_tile[kFp8Pipe ? kTileBytes : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw0[kFp8Pipe ? kRawTileBytes + 1024 : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw1[kFp8Pipe ? kRawTileBytes + 1024 : 1024];
     // sparse index words of four tiles (tile x in slot x & 3), 64 per tile
-    __shared__ __attribute__((aligned(256))) int32_t lds_ring[kPvLoads && SPARSE ? 4 * 64 : 1];
+    __shared__ __attribute__((aligned(256))) int32_t lds_ring[kFp8Pipe && SPARSE ? 4 * 64 : 1];
     char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                      (unsigned)(ix_row0 + k * kBlock + (opaque(lane) & 63)) * 4u);
         };
         unsigned idx_a = kOOB, idx_b = kOOB, idx_c = kOOB;
-        if constexpr (kPvLoads && SPARSE) {
+        if constexpr (kFp8Pipe && SPARSE) {
             ring_load(t0);
             ring_load(t0 + 1);
             ring_load(t0 + 2);
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             return mask;
         };
-        const int n_dma = kPvLoads ? 11 : (FP8 ? (wave == 0 ? 11 : 10) : 18);
+        const int n_dma = kFp8Pipe ? 11 : (FP8 ? (wave == 0 ? 11 : 10) : 18);
 
         // FP8, 128-head groups: chunk j (0..10) of a tile's raw image; chunk
         // c = wave + 4 j holds 16-byte units kk = 64 c + lane (token kk / 41,
@@ -413,13 +413,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
 
         // ------------------------------------------------ compute one tile
-        // Side work between MFMAs (tile loads; see the tile pipeline):
-        //   side(0, j), j = 0..17, after the score MFMAs of k-step 2 j (j < 17)
-        //     or 33 (j = 17), when the first tag is true;
-        //   side(1, j), j = 0..10, after PV MFMA 6 j, when the second tag is true.
-        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto qk_tag, auto pv_tag, auto&& side) {
-            constexpr bool kSideQk = decltype(qk_tag)::value;
-            constexpr bool kSide = decltype(pv_tag)::value;
+        // Side work between the score MFMAs (tile loads; see the tile
+        // pipeline): side(j), j = 0..17, after the MFMAs of k-step 2 j (j < 17)
+        // or 33 (j = 17), when the tag is true.
+        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto side_tag, auto&& side) {
+            constexpr bool kSideQk = decltype(side_tag)::value;
             if constexpr (R32) {
                 // S^T = K Q^T on 32x32x16 MFMAs: two accumulation chains (the two
                 // token blocks for V128; even/odd k-steps of the one block for V64).
@@ -444,8 +442,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                         sc[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][bb], qreg[kk], sc[ch], 0, 0, 0);
                     }
                     if constexpr (kSideQk) {
-                        if (kk < 33 && kk % 2 == 0) side(0, kk / 2);
-                        else if (kk == 33) side(0, 17);
+                        if (kk < 33 && kk % 2 == 0) side(kk / 2);
+                        else if (kk == 33) side(17);
                     }
                 }
                 // keep the read-ahead: reads first, then (NB MFMA, NB reads) groups
@@ -531,15 +529,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int j = 0; j < kVF; ++j) va[j] = vread(j);
                 mfma_fence();  // pb (VALU) -> MFMA operand
-                constexpr int kSideEvery = 6, kSideN = 11;
                 #pragma unroll
                 for (int n = 0; n < NPV; ++n) {
                     if (n + kVF < NPV) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
                     const int cl = n >> 4, d = n & 15;
                     mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[cl]);
-                    if constexpr (kSide) {
-                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN) side(1, n / kSideEvery);
-                    }
                 }
                 mfma_fence();  // MFMA results -> later AGPR reads / scaling
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVF, 0);
@@ -547,14 +541,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 for (int n = 0; n < NPV - kVF; ++n) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    if constexpr (kSide) {
-                        // a load every kSideEvery MFMAs, its address VALU two per
-                        // MFMA in the slots before it
-                        if (n % kSideEvery == 0 && n / kSideEvery < kSideN)
-                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                        else
-                            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-                    }
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, kVF, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -630,15 +616,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         };
 
         // ------------------------------------------------ tile pipeline
-        if constexpr (kPvLoads) {
+        if constexpr (kFp8Pipe) {
           if (t0 <= t1) {
             // Tile k: wait for its raw image, dequantise it into the bf16 tile,
             // then compute it while tile k + 2's loads (into the raw buffer just
-            // dequantised) go out between its PV MFMAs, one every 6 MFMAs: a CU
-            // takes an LDS-direct load every ~25 cycles, so loads issued back to
-            // back stall the issuing waves, but spread this way they do not.
-            // The loop is unrolled by two so that each raw buffer has a fixed
-            // role in each half.
+            // dequantised) go out between its score MFMAs, one every two
+            // k-steps per wave: a CU takes an LDS-direct load every ~25 cycles,
+            // so loads issued back to back stall the issuing waves, but spread
+            // this way they do not. (Between the PV MFMAs instead: 2 % slower.)
             char LDS_AS* tile = (char LDS_AS*)lds_tile;
             char LDS_AS* raw0 = (char LDS_AS*)lds_raw0;
             char LDS_AS* raw1 = (char LDS_AS*)lds_raw1;
@@ -687,9 +672,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // chunk j is issued with the address computed after chunk j - 1,
                 // so its VALU fills the MFMA slots between the two loads
                 ChunkAddr ca = chunk_addr(0, tn);
-                compute_tile(tile, mask_a, std::false_type{}, std::true_type{}, [&](int, int j) {
-                    chunk_issue(j, cur, ca);
-                    if (j + 1 < 11) ca = chunk_addr(j + 1, tn);
+                compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
+                    if (j < 11) {
+                        chunk_issue(j, cur, ca);
+                        if (j + 1 < 11) ca = chunk_addr(j + 1, tn);
+                    }
                 });
                 idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
                 mask_a = mask_b; mask_b = tn.mask;
@@ -744,7 +731,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const TileSrc tn = (k + 1 <= t1) ? tile_src(k + 1, idx_n) : none;
                 unsigned rows[2];
                 tile_rows(tn, rows);
-                compute_tile(cur, mask_a, std::true_type{}, std::false_type{}, [&](int, int j) { qk_chunk(j, nxt, rows); });
+                compute_tile(cur, mask_a, std::true_type{}, [&](int j) { qk_chunk(j, nxt, rows); });
                 mask_a = tn.mask;
                 idx_n = idx_f;
             }
@@ -783,9 +770,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     dequant(cur, ctile);
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
-                    compute_tile(ctile, mask_a, std::false_type{}, std::false_type{}, [](int, int) {});
+                    compute_tile(ctile, mask_a, std::false_type{}, [](int) {});
                 } else {
-                    compute_tile(cur, mask_a, std::false_type{}, std::false_type{}, [](int, int) {});
+                    compute_tile(cur, mask_a, std::false_type{}, [](int) {});
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                 }
