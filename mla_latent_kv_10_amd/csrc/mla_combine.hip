@@ -15,6 +15,8 @@
 //   RG = 16: row-major [row][512].
 // Each thread owns one row and a fixed set of float4s; consecutive threads
 // read consecutive float4s of a slot.
+#include <type_traits>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -88,34 +90,45 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     f32x4 acc[M::kVec];
     #pragma unroll
     for (int j = 0; j < M::kVec; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < n; k0 += kU) {
-        float lv[kU];
-        f32x4 v[kU][M::kVec];
-        #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const bool in = k0 + u < n;
-            lv[u] = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+    // Each partial is read exactly once. With three or more splits the loads
+    // are non-temporal (measured faster); with two (long sequences, many
+    // workgroups) the default policy measured faster.
+    auto merge = [&](auto nt_tag) {
+        constexpr bool NT = decltype(nt_tag)::value;
+        for (int k0 = 0; k0 < n; k0 += kU) {
+            float lv[kU];
+            f32x4 v[kU][M::kVec];
             #pragma unroll
-            for (int j = 0; j < M::kVec; ++j)
-                v[u][j] = in ? base[(int64_t)(k0 + u) * kSlot4 + f4[j]] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        float mc = m;
-        #pragma unroll
-        for (int u = 0; u < kU; ++u) mc = fmaxf(mc, lv[u]);
-        if (mc == -INFINITY) continue;  // nothing attended so far
-        const float r = (m == -INFINITY) ? 0.f : __expf(m - mc);
-        s *= r;
-        #pragma unroll
-        for (int j = 0; j < M::kVec; ++j) acc[j] *= r;
-        #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const float wgt = lv[u] == -INFINITY ? 0.f : __expf(lv[u] - mc);
-            s += wgt;
+            for (int u = 0; u < kU; ++u) {
+                const bool in = k0 + u < n;
+                lv[u] = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+                #pragma unroll
+                for (int j = 0; j < M::kVec; ++j) {
+                    const f32x4* src = &base[(int64_t)(k0 + u) * kSlot4 + f4[j]];
+                    if constexpr (NT) v[u][j] = in ? __builtin_nontemporal_load(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    else v[u][j] = in ? *src : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            float mc = m;
             #pragma unroll
-            for (int j = 0; j < M::kVec; ++j) acc[j] += wgt * v[u][j];
+            for (int u = 0; u < kU; ++u) mc = fmaxf(mc, lv[u]);
+            if (mc == -INFINITY) continue;  // nothing attended so far
+            const float r = (m == -INFINITY) ? 0.f : __expf(m - mc);
+            s *= r;
+            #pragma unroll
+            for (int j = 0; j < M::kVec; ++j) acc[j] *= r;
+            #pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const float wgt = lv[u] == -INFINITY ? 0.f : __expf(lv[u] - mc);
+                s += wgt;
+                #pragma unroll
+                for (int j = 0; j < M::kVec; ++j) acc[j] += wgt * v[u][j];
+            }
+            m = mc;
         }
-        m = mc;
-    }
+    };
+    if (n >= 3) merge(std::true_type{});
+    else merge(std::false_type{});
     // no split attended anything (or no split at all): o = 0, lse = -inf
     const bool empty = m == -INFINITY;
     const float inv = empty ? 0.f : 1.f / s;
