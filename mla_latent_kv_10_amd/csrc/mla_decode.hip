@@ -56,8 +56,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // Dense bf16 with 128-head groups issues each tile's loads between the
     // score MFMAs of the tile before it (see the tile pipeline).
     constexpr bool kQkLoads = !FP8 && !SPARSE && VAR == kV128;
-    // Both read dense block-table words as scalar loads.
-    constexpr bool kScalarIdx = (kFp8Pipe || kQkLoads) && !SPARSE;
+    // Every dense variant reads block-table words as scalar loads and issues
+    // its tile loads as inline asm the compiler does not track, so that no
+    // compiler wait for a load in flight lands inside the tile loop (in the
+    // generic pipeline below, such a wait before the transposed V reads made
+    // each tile wait for the next one's loads).
+    constexpr bool kScalarIdx = !SPARSE;
     __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8Pipe ? 1024 : S::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_tile[kFp8Pipe ? kTileBytes : 1024];
     __shared__ __attribute__((aligned(1024))) char lds_raw0[kFp8Pipe ? kRawTileBytes + 1024 : 1024];
@@ -198,6 +202,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // instructions per wave is fixed per variant (n_dma).
         // UNROLL: straight-line issue (the prologue), so the compiler's own
         // wait counts for loads issued before it (q) are exact.
+        const u32x4 kv_words = make_rsrc_words(p.kv, p.row_bytes, (unsigned)p.num_rows);
+        // One 1 KB chunk of a tile into LDS: dense -> untracked asm load (see
+        // kScalarIdx); sparse -> the builtin (its index words are VMEM loads
+        // held in registers, which the compiler must be able to count).
+        auto tile_load = [&](char LDS_AS* dst, unsigned row, unsigned voff, int soff) {
+            if constexpr (!SPARSE) dma16_asm(kv_words, lds_addr(dst), row, voff, soff);
+            else dma16(kv_rsrc, dst, row, voff, soff);
+        };
+
         // Where tile k's rows come from, given its index word: dense -> the
         // page's first cache row and the attended token count; sparse -> each
         // lane's (token's) validated cache row. mask: bit t set = token t attended.
@@ -241,11 +254,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if constexpr (UNROLL) {
                         #pragma unroll
                         for (int ug = 0; ug < 9; ++ug)
-                            dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                            tile_load(dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
                     } else {
                         #pragma unroll 1
                         for (int ug = 0; ug < 9; ++ug)
-                            dma16(kv_rsrc, dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                            tile_load(dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
                     }
                 };
                 if constexpr (UNROLL) {
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
                     else row = dense_row(page0, n_valid, t);
-                    dma16(kv_rsrc, dst + (c << 10), row, (unsigned)(u << 4), 0);
+                    tile_load(dst + (c << 10), row, (unsigned)(u << 4), 0);
                     u += 10;
                     t += 6;
                     if (u >= kRawUnits) { u -= kRawUnits; t += 1; }
@@ -290,7 +303,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // unit kk % 41). Branch-free, so it can sit between MFMAs: waves 1..3
         // have no chunk 10 and load nothing into the spare 1 KB after the tile
         // instead, and a tile past the segment (no rows) loads nothing.
-        const u32x4 kv_words = make_rsrc_words(p.kv, p.row_bytes, (unsigned)p.num_rows);
         struct ChunkAddr {
             unsigned row, voff;
         };
@@ -756,12 +768,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 char LDS_AS* cur = odd ? stage1 : stage0;
                 const unsigned idx_d = fetch_index(k + 3);
                 // VMEM instructions this wave issued after tile k's DMA (a
-                // lower bound is safe: it only waits longer).
+                // lower bound is safe: it only waits longer): tile k + 1's loads,
+                // and for the sparse index (VMEM) the words of k + 2 and k + 3
+                // (dense index words are scalar loads).
                 int after = 0;
                 if (k + 1 <= t1) {
                     after += n_dma;
-                    if (k > t0 && k + 2 <= t1) after += 1;
-                    if (k + 3 <= t1) after += 1;
+                    if (SPARSE && k > t0 && k + 2 <= t1) after += 1;
+                    if (SPARSE && k + 3 <= t1) after += 1;
                 }
                 wait_vm(after);
                 block_sync_lds();
