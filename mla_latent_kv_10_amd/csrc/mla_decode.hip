@@ -13,7 +13,10 @@
 //    each lane names its token's row; a masked token gets an out-of-range
 //    index and the hardware writes zeros, so masked rows are never read.
 //    Two tiles are in flight (double buffering); waits are explicit vmcnt
-//    counts plus raw s_barrier, so prefetches stay outstanding.
+//    counts plus raw s_barrier, so prefetches stay outstanding. With 128-head
+//    groups the next tile's loads are spread over the current tile's score
+//    MFMAs: a CU accepts an LDS-direct load only every ~25 cycles, so loads
+//    issued back to back stall the waves issuing them.
 //  * The bf16 tile sits in LDS as 72 chunks of 1 KB (8 tokens x 8 16-byte
 //    units), with the unit index XOR-swizzled by (token/2) so that 16 lanes
 //    reading 16 tokens at one unit hit 16 distinct bank groups.
@@ -46,12 +49,11 @@ template <bool FP8, bool SPARSE, int VAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     using S = Smem<FP8>;
     // FP8 with 128-head groups spreads each tile's loads over the score MFMAs
-    // of the tile two ahead (see the tile pipeline). Its bf16 tile and its two raw
-    // tiles are separate LDS arrays, so the compiler can tell the loads in
-    // flight from the operand reads and waits only where a buffer is reused;
-    // each raw array has a spare 1 KB after the tile for the padding load of
-    // waves 1..3 (41 chunks over 4 waves). The other variants share one array
-    // (the 64- and 16-head ones reuse all of it for their end-of-segment merge).
+    // of the tile two ahead (see the tile pipeline). Its bf16 tile and its two
+    // raw tiles are separate LDS arrays; each raw array has a spare 1 KB after
+    // the tile for the padding load of waves 1..3 (41 chunks over 4 waves). The
+    // other variants use one array (the 64- and 16-head ones reuse all of it
+    // for their end-of-segment merge).
     constexpr bool kFp8Pipe = FP8 && VAR == kV128;
     // Dense bf16 with 128-head groups issues each tile's loads between the
     // score MFMAs of the tile before it (see the tile pipeline).
@@ -98,10 +100,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         const int64_t qrow0 = ((int64_t)sg.b * p.s_q + sg.i) * p.h_q;  // row index of head 0
         const int32_t* idx_row = SPARSE ? p.indices + ((int64_t)sg.b * p.s_q + sg.i) * p.topk : nullptr;
 
-        // Index word of tile k, one VMEM load per wave: sparse -> lane l holds
-        // the raw index entry of token l (range-checked where the tile is
-        // issued); dense -> every lane holds the tile's page id. `kmax` bounds
-        // the block-table read; words past the segment's last tile are never used.
+        // Index word of tile k: sparse -> a VMEM load, lane l holds the raw index
+        // entry of token l (range-checked where the tile is issued); dense -> a
+        // scalar load of the tile's page id. `kmax` bounds the block-table read;
+        // words past the segment's last tile are never used.
         auto load_index = [&](int k, int kmax) -> unsigned {
             unsigned r = kOOB;
             if (k <= kmax) {
@@ -197,11 +199,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             return (blk >= 0 && (int64_t)blk * kBlock < (int64_t)p.num_rows) ? blk * kBlock : -1;
         };
 
-        // Issue the DMA of tile k into LDS region `dst`; returns the tile's
-        // validity mask (bit t set = token t attended). The number of VMEM
-        // instructions per wave is fixed per variant (n_dma).
-        // UNROLL: straight-line issue (the prologue), so the compiler's own
-        // wait counts for loads issued before it (q) are exact.
         const u32x4 kv_words = make_rsrc_words(p.kv, p.row_bytes, (unsigned)p.num_rows);
         // One 1 KB chunk of a tile into LDS: dense -> untracked asm load (see
         // kScalarIdx); sparse -> the builtin (its index words are VMEM loads
@@ -233,6 +230,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             return ts;
         };
+        // Issue the loads of tile k into LDS region `dst` back to back (the
+        // 64- and 16-head pipelines); returns the tile's validity mask. The
+        // number of VMEM instructions per wave is fixed per variant (n_dma).
+        // UNROLL: straight-line issue (the prologue).
         auto issue_tile = [&](auto unroll_tag, int k, char LDS_AS* dst, unsigned word) -> uint64_t {
             constexpr bool UNROLL = decltype(unroll_tag)::value;
             const TileSrc ts = tile_src(k, word);
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             }
             return mask;
         };
-        const int n_dma = kFp8Pipe ? 11 : (FP8 ? (wave == 0 ? 11 : 10) : 18);
+        const int n_dma = FP8 ? (wave == 0 ? 11 : 10) : 18;
 
         // FP8, 128-head groups: chunk j (0..10) of a tile's raw image; chunk
         // c = wave + 4 j holds 16-byte units kk = 64 c + lane (token kk / 41,

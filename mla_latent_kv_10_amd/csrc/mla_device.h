@@ -15,17 +15,11 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;  // exponent reference moves when a row max grows by > 2^8
 constexpr unsigned kOOB = 0xFFFFFFFFu;
 
 // ---------------------------------------------------------------- LDS layout
-
-// Byte offset of (token t, 16-byte unit u) inside a swizzled bf16 tile.
-__device__ __forceinline__ int tile_off(int t, int u) {
-    return (((t >> 3) * 9 + (u >> 3)) << 10) + ((((t & 7) << 3) | ((u & 7) ^ ((t >> 1) & 7))) << 4);
-}
 
 template <bool FP8>
 struct Smem {
