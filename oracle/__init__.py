@@ -22,3 +22,4 @@ from .mla_oracle import (  # noqa: F401
     lse_merge,
 )
 from .schedule import split_schedule, tile_counts  # noqa: F401
+from .quantize import f32_to_e4m3fn_codes, quantize_rows, append_rows  # noqa: F401

@@ -127,3 +127,69 @@ def test_fp8_group_mutant_is_caught(monkeypatch):
 def test_bf16_rounding_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(tf, "f32_to_bf16_bits", _bf16_truncate)
     assert _fails(tf.test_bf16_rne_matches_torch)
+
+
+# ---- the FP8 cache writer -------------------------------------------------
+
+import oracle.quantize as oq  # noqa: E402
+import tests.test_oracle_quantize as tq  # noqa: E402
+
+_real_codes = oq.f32_to_e4m3fn_codes
+_real_quantize = oq.quantize_rows
+
+
+def _codes_ties_away(y):
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    hi = np.minimum(np.searchsorted(oq._POS_VALUES, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    pick_hi = (oq._POS_VALUES[hi] - a) <= (a - oq._POS_VALUES[lo])
+    return np.where(pick_hi, hi, lo).astype(np.uint8) | (np.signbit(y).astype(np.uint8) << np.uint8(7))
+
+
+def _codes_unsigned_zero(y):
+    c = _real_codes(y)
+    return np.where((c & 0x7F) == 0, np.uint8(0), c).astype(np.uint8)
+
+
+def _quantize_scale_over_256(src):
+    bits = np.asarray(src, dtype=np.uint16)
+    n = bits.shape[0]
+    lat = (bits[:, :512].astype(np.uint32) << np.uint32(16)).view(np.float32).reshape(n, 4, 128)
+    amax = np.abs(lat).max(axis=2)
+    scale = np.where(amax == 0, np.float32(1), amax / np.float32(256)).astype(np.float32)
+    y = np.clip((lat / scale[:, :, None]).astype(np.float32), -448, 448)
+    out = _real_quantize(bits)
+    out[:, :512] = _real_codes(y).reshape(n, 512)
+    out[:, 512:528] = scale.astype("<f4").view(np.uint8).reshape(n, 16)
+    return out
+
+
+def _quantize_scales_big_endian(src):
+    out = _real_quantize(src)
+    out[:, 512:528] = out[:, 512:528].reshape(-1, 4, 4)[:, :, ::-1].reshape(-1, 16)
+    return out
+
+
+def _quantize_rope_from_latent(src):
+    out = _real_quantize(src)
+    bits = np.asarray(src, dtype=np.uint16)
+    out[:, 528:] = bits[:, :64].astype("<u2").view(np.uint8).reshape(-1, 128)
+    return out
+
+
+QUANTIZE_PINS = [tq.test_codes_match_torch_cast_on_every_bf16_value_in_range, tq.test_hand_worked_ties_and_signs,
+                 tq.test_golden_row, tq.test_matches_the_input_generators_writer, tq.test_round_trip_within_e4m3_bound]
+
+
+@pytest.mark.parametrize("mutant", [_codes_ties_away, _codes_unsigned_zero])
+def test_e4m3_rounding_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(tq, "f32_to_e4m3fn_codes", mutant)
+    monkeypatch.setattr(oq, "f32_to_e4m3fn_codes", mutant)
+    assert any(_fails(p) for p in QUANTIZE_PINS)
+
+
+@pytest.mark.parametrize("mutant", [_quantize_scale_over_256, _quantize_scales_big_endian, _quantize_rope_from_latent])
+def test_writer_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(tq, "quantize_rows", mutant)
+    assert any(_fails(p) for p in QUANTIZE_PINS)
