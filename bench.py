@@ -54,29 +54,49 @@ def algorithmic_counts(w):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.md")
-KERNEL_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_common.h", "build.py")
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_kernel_hbm_traffic.md")
+QUANT_ROW_BYTES = 1152 + 4 + 656  # bf16 row in, its slot, the 656-byte row out
+KERNEL_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_common.h")
+QUANT_SOURCES = ("mla_quantize.hip", "mla_quantize.h", "mla_common.h")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the split kernel's sources and build flags (first 16 hex digits)."""
+def source_hash(names=KERNEL_SOURCES, compiled="mla_decode.hip") -> str:
+    """sha256 over a kernel's sources and its compile flags (first 16 hex digits).
+
+    Include paths are left out of the flags so the value does not depend on where the tree sits.
+    """
     import hashlib
 
+    from mla_latent_kv_10_amd import build as B
+
     h = hashlib.sha256()
-    pkg = os.path.join(ROOT, "mla_latent_kv_10_amd")
-    for name in KERNEL_SOURCES:
-        path = os.path.join(pkg, "csrc", name) if name != "build.py" else os.path.join(pkg, name)
-        with open(path, "rb") as f:
+    for name in names:
+        with open(os.path.join(B.CSRC, name), "rb") as f:
             h.update(f.read())
+    flags = B.COMMON_FLAGS + B.EXTRA_FLAGS.get(compiled, [])
+    kept = [f for i, f in enumerate(flags) if f != "-I" and not (i > 0 and flags[i - 1] == "-I")]
+    h.update("\0".join(kept).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, num_parts: int):
-    """HBM bytes per split-kernel launch from the committed counter summary, or
-    None when there is none for this workload or the kernel changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
+def kernel_source_hash() -> str:
+    """Hash of the split kernel's sources and flags."""
+    return source_hash(KERNEL_SOURCES, "mla_decode.hip")
+
+
+def quantize_source_hash() -> str:
+    """Hash of the FP8 cache writer's sources and flags."""
+    return source_hash(QUANT_SOURCES, "mla_quantize.hip")
+
+
+def measured_traffic(workload: str, num_parts, want=None, path=None):
+    """HBM bytes per kernel launch from the committed counter summary, or None
+    when there is none for this workload or the kernel changed since."""
+    path = path or TRAFFIC_FILE
+    if not os.path.exists(path):
         return None
-    want = kernel_source_hash()
-    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+    want = want or kernel_source_hash()
+    for line in open(path, encoding="utf-8"):
         # machine-readable rows: "traffic | <workload> | <num_parts> | <bytes> | <source hash>"
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) == 5 and cells[0] == "traffic" and cells[1] == workload and cells[2] == str(num_parts):
@@ -156,6 +176,95 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+QUANT_METRIC = "FP8 cache write GB/s (bf16 rows in, 656-byte FP8 rows out), 1 GPU"
+
+
+def quantize_workload(batch: int = 64, seqlen: int = 8192, seed: int = 0):
+    """Rows of a whole FP8 cache (batch x seqlen tokens) into shuffled pages: (name, src bf16 [n, 576], slots int32 [n])."""
+    import torch
+
+    g = torch.Generator().manual_seed(seed)
+    n = batch * seqlen
+    src = torch.randn(n, 576, generator=g).to(torch.bfloat16)
+    pages = torch.randperm(n // 64, generator=g).to(torch.int32)
+    t = torch.arange(n, dtype=torch.int32)
+    slots = pages[t // 64] * 64 + t % 64
+    name = f"fp8 cache write: {n} rows ({batch} x {seqlen} tokens) into {n // 64} shuffled pages"
+    return name, src, slots
+
+
+def quantize_cpu_baseline(src, seconds: float):
+    """The oracle's writer on the host over a bounded sample of the same rows."""
+    import numpy as np
+    import torch
+
+    from oracle import quantize_rows
+
+    bits = src.view(torch.int16).numpy().view(np.uint16)
+    chunk = 4096
+    done = 0
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        s0 = (k * chunk) % (bits.shape[0] - chunk)
+        quantize_rows(bits[s0:s0 + chunk])
+        done += chunk
+        k += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done * QUANT_ROW_BYTES / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows of the same workload in chunks of {chunk}, NumPy float32, {dt:.1f} s"}
+
+
+def bench_quantize(args):
+    """Time mla_quantize_fp8_append writing a whole FP8 cache."""
+    import torch
+
+    import mla_latent_kv_10_amd as mla
+
+    dev = torch.device("cuda:0")
+    name, src_cpu, slots_cpu = quantize_workload()
+    n = src_cpu.shape[0]
+    src, slots = src_cpu.to(dev), slots_cpu.to(dev)
+    kv = torch.zeros((n // 64, 64, 656), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)  # the binding launches on torch's current stream
+    for _ in range(max(1, args.warmup)):
+        mla.quantize_fp8_append(src, slots, kv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        mla.quantize_fp8_append(src, slots, kv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    algo = n * QUANT_ROW_BYTES
+    gbps = algo / (ms * 1e-3) / 1e9
+    out = {
+        "metric": QUANT_METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp8-e4m3 + fp32 scales out",
+        "data": "synthetic",
+        "config": {"workload": name, "rows": n, "pages": n // 64},
+        "kernel_source_hash": quantize_source_hash(),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(name, "-", quantize_source_hash(), QUANT_TRAFFIC_FILE),
+                     "kernel": "quantize_kernel (mla_quantize_fp8_append)", "kernel_ms": round(ms, 5),
+                     "per_launch": {"bytes": algo, "rows": n, "bytes_per_row": QUANT_ROW_BYTES}},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = quantize_cpu_baseline(src_cpu, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +275,8 @@ def main():
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("decode", "quantize"), default="decode",
+                    help="decode: the decode step (default); quantize: the FP8 cache writer")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -180,6 +291,10 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(1, args.steps))
+        return
+    if args.op == "quantize":
+        torch.cuda.set_device(0)
+        bench_quantize(args)
         return
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")

@@ -184,6 +184,31 @@ int mla_decode_splits(const mla_decode_args* args, void* stream);
  */
 int mla_combine(const mla_decode_args* args, void* stream);
 
+/*
+ * FP8 cache writer (quantise on write): turns n bf16 cache rows into the
+ * 656-byte FP8 layout of [Guide] §"FP8 缓存怎么把 KV 压掉四成" and stores
+ * row i at absolute cache row slots[i] (= page * 64 + offset, the row
+ * numbering sparse indices use). [Guide] §"容易踩的坑" is why the writer must
+ * match this layout exactly.
+ *   src    device bf16 [n, 576]: latent (512) then RoPE (64), the row a bf16
+ *          cache would hold; 16-byte aligned; read only. Values are finite.
+ *   slots  device int32 [n]; -1, or any value outside [0, num_blocks * 64),
+ *          writes nothing. Two rows aimed at one slot race (one of them lands).
+ *   kv     device [num_blocks, 64, 656] bytes, 16-byte aligned; only the
+ *          addressed rows are written.
+ * Per 128 latent values: scale = amax / 448 in fp32 (1 if the group is all
+ * zero; [Walkthrough] §三 for e4m3's 448 maximum), code = e4m3 (OCP, finite
+ * only) round-to-nearest-even of clamp(x / scale, -448, 448); both divisions
+ * are IEEE fp32. Bytes [0, 512) codes, [512, 528) the four scales
+ * (little-endian fp32), [528, 656) the RoPE bf16 values unchanged.
+ * n == 0 enqueues nothing. Errors: MLA_ERR_INVALID (negative n, NULL or
+ * misaligned pointers, num_blocks < 1), MLA_ERR_UNSUPPORTED (n >= 2^31 or
+ * num_blocks * 64 >= 2^31), MLA_ERR_HIP (launch failure). Asynchronous on
+ * `stream`; allocates nothing.
+ */
+int mla_quantize_fp8_append(const void* src, const int32_t* slots, int64_t n, void* kv, int64_t num_blocks,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

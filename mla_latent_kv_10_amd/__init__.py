@@ -73,6 +73,7 @@ EXPORTS = (
     "mla_decode_with_kvcache",
     "mla_decode_splits",
     "mla_combine",
+    "mla_quantize_fp8_append",
 )
 
 _lib = None
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_with_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_decode_splits.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    L.mla_quantize_fp8_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_void_p]
     for name in EXPORTS:
         getattr(L, name).restype = ctypes.c_char_p if name == "mla_last_error" else ctypes.c_int
     _lib = L
@@ -245,3 +248,18 @@ def mla_decode_splits(args: MlaDecodeArgs, stream: int) -> None:
 def mla_combine(args: MlaDecodeArgs, stream: int) -> None:
     """Run only the split merge for a prepared argument block."""
     check(lib().mla_combine(ctypes.byref(args), stream))
+
+
+def quantize_fp8_append(src, slots, kv) -> None:
+    """Quantise bf16 rows src [n, 576] into the FP8 cache kv [num_blocks, 64, 656] (uint8) at rows slots [n]."""
+    torch = _torch()
+    _require_gpu(src, slots, kv)
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.shape[1] != 576:
+        raise ValueError("src must be bfloat16 [n, 576]")
+    if slots.dtype != torch.int32 or slots.shape != (src.shape[0],):
+        raise ValueError("slots must be int32 [n]")
+    if kv.dtype != torch.uint8 or kv.dim() != 3 or tuple(kv.shape[1:]) != (64, 656):
+        raise ValueError("kv must be uint8 [num_blocks, 64, 656]")
+    check(lib().mla_quantize_fp8_append(src.data_ptr(), slots.data_ptr(), src.shape[0], kv.data_ptr(), kv.shape[0],
+                                        _stream_handle(src.device)))
+

@@ -8,6 +8,7 @@
 
 #include "mla.h"
 #include "mla_common.h"
+#include "mla_quantize.h"
 
 namespace {
 
@@ -207,6 +208,28 @@ int mla_combine(const mla_decode_args* args, void* stream) {
     if (st) return st;
     hipError_t e = mla::launch_combine(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_quantize_fp8_append(const void* src, const int32_t* slots, int64_t n, void* kv, int64_t num_blocks,
+                            void* stream) {
+    if (n < 0) return fail(MLA_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+    if (n >= ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "n must be < 2^31 rows per call");
+    if (num_blocks < 1) return fail(MLA_ERR_INVALID, "num_blocks must be >= 1");
+    if (num_blocks * (int64_t)mla::kBlock >= ((int64_t)1 << 31))
+        return fail(MLA_ERR_UNSUPPORTED, "num_blocks * 64 must be < 2^31");
+    if (n == 0) return ok();
+    if (!src || !slots || !kv) return fail(MLA_ERR_INVALID, "src, slots and kv must be non-NULL");
+    if (!aligned(src, 16) || !aligned(kv, 16) || !aligned(slots, 4))
+        return fail(MLA_ERR_INVALID, "src and kv must be 16-byte aligned, slots 4-byte aligned");
+    mla::QuantParams p;
+    p.src = static_cast<const uint16_t*>(src);
+    p.slots = slots;
+    p.kv = static_cast<uint8_t*>(kv);
+    p.n = n;
+    p.num_rows = (int)(num_blocks * mla::kBlock);
+    hipError_t e = mla::launch_quantize(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
     return ok();
 }
 

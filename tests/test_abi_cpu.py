@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "mla.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -161,3 +161,31 @@ def test_null_args_and_metadata_errors():
     assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 256, 0, FAKE, None) == m.MLA_ERR_INVALID
     assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 0, FAKE, FAKE, None) == m.MLA_ERR_INVALID
     assert b"num_parts" in L.mla_last_error()
+
+
+QUANT_CASES = [
+    (dict(n=-1), m.MLA_ERR_INVALID, "n must be"),
+    (dict(n=1 << 31), m.MLA_ERR_UNSUPPORTED, "2^31"),
+    (dict(num_blocks=0), m.MLA_ERR_INVALID, "num_blocks"),
+    (dict(num_blocks=1 << 26), m.MLA_ERR_UNSUPPORTED, "2^31"),
+    (dict(src=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(slots=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(kv=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(src=FAKE + 8), m.MLA_ERR_INVALID, "aligned"),
+    (dict(kv=FAKE + 4), m.MLA_ERR_INVALID, "aligned"),
+    (dict(slots=FAKE + 2), m.MLA_ERR_INVALID, "aligned"),
+]
+
+
+@pytest.mark.parametrize("over,status,text", QUANT_CASES)
+def test_quantize_rejects_bad_arguments(over, status, text):
+    kw = dict(src=FAKE, slots=FAKE, n=8, kv=FAKE, num_blocks=4)
+    kw.update(over)
+    st = m.lib().mla_quantize_fp8_append(kw["src"], kw["slots"], kw["n"], kw["kv"], kw["num_blocks"], None)
+    assert st == status
+    assert text in m.lib().mla_last_error().decode()
+
+
+def test_quantize_with_no_rows_enqueues_nothing():
+    # n == 0 returns before any HIP call, so it succeeds without a GPU and with NULL buffers
+    assert m.lib().mla_quantize_fp8_append(0, 0, 0, 0, 4, None) == m.MLA_OK

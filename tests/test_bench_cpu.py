@@ -45,3 +45,15 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_writer_traffic_row_and_cpu_leg():
+    name, src, slots = bench.quantize_workload(batch=2, seqlen=4096)
+    assert src.shape == (8192, 576) and sorted(slots.tolist()) == list(range(8192))
+    # the committed writer row is keyed by the writer's own source hash
+    full = "fp8 cache write: 524288 rows (64 x 8192 tokens) into 8192 shuffled pages"
+    got = bench.measured_traffic(full, "-", bench.quantize_source_hash(), bench.QUANT_TRAFFIC_FILE)
+    assert got is not None and got >= 524288 * bench.QUANT_ROW_BYTES
+    assert bench.measured_traffic(full, "-", "0" * 16, bench.QUANT_TRAFFIC_FILE) is None
+    leg = bench.quantize_cpu_baseline(src, 0.2)
+    assert leg["kind"] == "oracle" and leg["unit"] == "GB/s" and leg["value"] > 0
