@@ -23,3 +23,4 @@ from .mla_oracle import (  # noqa: F401
 )
 from .schedule import split_schedule, tile_counts  # noqa: F401
 from .quantize import f32_to_e4m3fn_codes, quantize_rows, append_rows  # noqa: F401
+from .absorb import absorb_q, unabsorb_o  # noqa: F401

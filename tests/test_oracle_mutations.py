@@ -193,3 +193,41 @@ def test_e4m3_rounding_mutants_are_caught(monkeypatch, mutant):
 def test_writer_mutants_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(tq, "quantize_rows", mutant)
     assert any(_fails(p) for p in QUANTIZE_PINS)
+
+
+# ---- the absorption products ---------------------------------------------
+
+import oracle.absorb as oa  # noqa: E402
+import tests.test_oracle_absorb as tab  # noqa: E402
+
+_real_absorb = oa.absorb_q
+_real_unabsorb = oa.unabsorb_o
+
+
+def _absorb_next_heads_weights(q_nope, q_rope, w_uk):
+    return _real_absorb(q_nope, q_rope, np.roll(np.asarray(w_uk), 1, axis=0))
+
+
+def _absorb_rope_dropped(q_nope, q_rope, w_uk):
+    out = _real_absorb(q_nope, q_rope, w_uk)
+    out[:, :, 512:] = 0
+    return out
+
+
+def _unabsorb_reshaped_weights(o_lat, w_uv):
+    w = oa._values(w_uv)
+    return _real_unabsorb(o_lat, w.reshape(w.shape[0], 512, 128).transpose(0, 2, 1))
+
+
+ABSORB_PINS = [tab.test_absorbed_layer_equals_explicit_multi_head_attention, tab.test_hand_built_weights_fix_the_orientation]
+
+
+@pytest.mark.parametrize("mutant", [_absorb_next_heads_weights, _absorb_rope_dropped])
+def test_absorb_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(tab, "absorb_q", mutant)
+    assert any(_fails(p) for p in ABSORB_PINS)
+
+
+def test_unabsorb_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(tab, "unabsorb_o", _unabsorb_reshaped_weights)
+    assert any(_fails(p) for p in ABSORB_PINS)
