@@ -265,6 +265,101 @@ def bench_quantize(args):
     print(json.dumps(out), flush=True)
 
 
+ABSORB_METRIC = "MLA absorption products GB/s (W^UK^T q^C before the decode, W^UV o after), 1 GPU"
+ABSORB_SOURCES = ("mla_absorb.hip", "mla_absorb.h", "mla_common.h")
+ABSORB_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "absorb_kernel_hbm_traffic.md")
+
+
+def absorb_counts(T: int, H: int):
+    """Algorithmic bytes and FLOPs of one absorb_q and one unabsorb_o launch (bf16 operands, each read once)."""
+    w = H * 128 * 512 * 2
+    absorb_bytes = w + T * H * (128 + 64 + 576) * 2
+    unabsorb_bytes = w + T * H * (512 + 128) * 2
+    flops = 2 * T * H * 128 * 512
+    return absorb_bytes, unabsorb_bytes, flops
+
+
+def bench_absorb(args):
+    """Time mla_absorb_q and mla_unabsorb_o at the FP8 causal workload's token count (64 x 2 tokens, 128 heads)."""
+    import torch
+
+    import mla_latent_kv_10_amd as mla
+
+    dev = torch.device("cuda:0")
+    B, s_q, H = 64, 2, 128
+    T = B * s_q
+    g = torch.Generator().manual_seed(0)
+    q_nope = torch.randn(T, H, 128, generator=g).to(torch.bfloat16).to(dev)
+    q_rope = torch.randn(T, H, 64, generator=g).to(torch.bfloat16).to(dev)
+    w_uk_t = (torch.randn(H, 512, 128, generator=g) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+    w_uv = (torch.randn(H, 128, 512, generator=g) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+    o_lat = torch.randn(T, H, 512, generator=g).to(torch.bfloat16).to(dev)
+    q = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)  # the binding launches on torch's current stream
+
+    def time_op(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_a = time_op(lambda: mla.absorb_q(q_nope, q_rope, w_uk_t, out=q))
+    ms_u = time_op(lambda: mla.unabsorb_o(o_lat, w_uv))
+    ba, bu, flops = absorb_counts(T, H)
+    gbps = (ba + bu) / ((ms_a + ms_u) * 1e-3) / 1e9
+    dom_ms, dom_bytes, dom = (ms_a, ba, "absorb_q") if ms_a >= ms_u else (ms_u, bu, "unabsorb_o")
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+    name = f"absorption products: T={T} tokens (B={B} x s_q={s_q}), H={H}"
+    out = {
+        "metric": ABSORB_METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_a + ms_u, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "heads": H},
+        "kernel_source_hash": source_hash(ABSORB_SOURCES, "mla_absorb.hip"),
+        "absorb_q_ms": round(ms_a, 5),
+        "unabsorb_o_ms": round(ms_u, 5),
+        "tflops": round(2 * flops / ((ms_a + ms_u) * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(name, dom, source_hash(ABSORB_SOURCES, "mla_absorb.hip"),
+                                                 ABSORB_TRAFFIC_FILE),
+                     "kernel": f"absorb_kernel ({dom})", "kernel_ms": round(dom_ms, 5),
+                     "per_launch": {"bytes": dom_bytes, "flop": flops}},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.absorb import absorb_q, unabsorb_o
+
+        bits = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view("uint16")  # noqa: E731
+        qn, qr, wk, ol, wv = bits(q_nope), bits(q_rope), bits(w_uk_t.transpose(1, 2)), bits(o_lat), bits(w_uv)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            sl = slice(done % T, done % T + 8)
+            absorb_q(qn[sl], qr[sl], wk)
+            unabsorb_o(ol[sl], wv)
+            done += 8
+        dt = time.perf_counter() - t0
+        per_tok = (ba + bu) / T  # bytes per token, weights amortised as on the GPU
+        out["cpu_baseline"] = {"value": round(done * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} tokens of the same inputs in groups of 8, float64 NumPy, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,8 +370,9 @@ def main():
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("decode", "quantize"), default="decode",
-                    help="decode: the decode step (default); quantize: the FP8 cache writer")
+    ap.add_argument("--op", choices=("decode", "quantize", "absorb"), default="decode",
+                    help="decode: the decode step (default); quantize: the FP8 cache writer; "
+                         "absorb: the absorption products around the decode")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -295,6 +391,10 @@ def main():
     if args.op == "quantize":
         torch.cuda.set_device(0)
         bench_quantize(args)
+        return
+    if args.op == "absorb":
+        torch.cuda.set_device(0)
+        bench_absorb(args)
         return
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")

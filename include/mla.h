@@ -209,6 +209,35 @@ int mla_combine(const mla_decode_args* args, void* stream);
 int mla_quantize_fp8_append(const void* src, const int32_t* slots, int64_t n, void* kv, int64_t num_blocks,
                             void* stream);
 
+/*
+ * Absorbed query ([Walkthrough] §六, the absorption passage): per token t and
+ * head i, q[t, i, 0:512] = W^UK_i^T q^C[t, i] and q[t, i, 512:576] = q^R[t, i],
+ * the 576-value query row the decode takes (its [batch, s_q, h_q, 576] q with
+ * tokens = batch * s_q, heads = h_q).
+ *   q_nope  device bf16 [tokens, heads, 128]: q^C
+ *   q_rope  device bf16 [tokens, heads, 64]: q^R, already rotated; copied
+ *   w_uk_t  device bf16 [heads, 512, 128]: per head the transpose of W^UK_i
+ *           (W^UK_i is 128 x 512, latent -> key); row n holds the 128
+ *           weights of latent dim n. Arranged once when weights are loaded.
+ *   q       device bf16 [tokens, heads, 576], written
+ * All pointers 16-byte aligned. fp32 accumulation, one round to bf16 (nearest
+ * even). tokens == 0 enqueues nothing. Errors: MLA_ERR_INVALID (negative
+ * tokens, heads < 1, NULL or misaligned pointers), MLA_ERR_UNSUPPORTED
+ * (heads > 4096, tokens * heads >= 2^31), MLA_ERR_HIP.
+ */
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, int64_t tokens, int heads, void* q,
+                 void* stream);
+
+/*
+ * Value up-projection after the decode ([Walkthrough] §六: o_i = W^UV_i times
+ * the attention-weighted sum of latents): out[t, i] = W^UV_i o[t, i].
+ *   o_latent  device bf16 [tokens, heads, 512]: the decode's o
+ *   w_uv      device bf16 [heads, 128, 512]: W^UV_i (latent -> value)
+ *   out       device bf16 [tokens, heads, 128], written
+ * Alignment, rounding, empty calls and errors as mla_absorb_q.
+ */
+int mla_unabsorb_o(const void* o_latent, const void* w_uv, int64_t tokens, int heads, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

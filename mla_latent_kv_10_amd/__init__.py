@@ -74,6 +74,8 @@ EXPORTS = (
     "mla_decode_splits",
     "mla_combine",
     "mla_quantize_fp8_append",
+    "mla_absorb_q",
+    "mla_unabsorb_o",
 )
 
 _lib = None
@@ -99,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.mla_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_quantize_fp8_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_int64, ctypes.c_void_p]
+    L.mla_absorb_q.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_unabsorb_o.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
     for name in EXPORTS:
         getattr(L, name).restype = ctypes.c_char_p if name == "mla_last_error" else ctypes.c_int
     _lib = L
@@ -262,4 +268,37 @@ def quantize_fp8_append(src, slots, kv) -> None:
         raise ValueError("kv must be uint8 [num_blocks, 64, 656]")
     check(lib().mla_quantize_fp8_append(src.data_ptr(), slots.data_ptr(), src.shape[0], kv.data_ptr(), kv.shape[0],
                                         _stream_handle(src.device)))
+
+
+def absorb_q(q_nope, q_rope, w_uk_t, out=None):
+    """Absorbed queries [T, H, 576] from q_nope [T, H, 128], q_rope [T, H, 64] and w_uk_t [H, 512, 128] (bf16)."""
+    torch = _torch()
+    _require_gpu(q_nope, q_rope, w_uk_t, out)
+    T, H, dn = q_nope.shape
+    for t, shape, label in ((q_nope, (T, H, 128), "q_nope"), (q_rope, (T, H, 64), "q_rope"),
+                            (w_uk_t, (H, 512, 128), "w_uk_t")):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape:
+            raise ValueError(f"{label} must be bfloat16 {list(shape)}")
+    if out is None:
+        out = torch.empty((T, H, 576), dtype=torch.bfloat16, device=q_nope.device)
+    elif out.dtype != torch.bfloat16 or out.numel() != T * H * 576:
+        raise ValueError("out must be bfloat16 with T * H * 576 elements")
+    check(lib().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk_t.data_ptr(), T, H, out.data_ptr(),
+                             _stream_handle(q_nope.device)))
+    return out
+
+
+def unabsorb_o(o_latent, w_uv):
+    """Per-head outputs [T, H, 128] = W^UV_h o_latent[t, h] from o_latent [T, H, 512] and w_uv [H, 128, 512] (bf16)."""
+    torch = _torch()
+    _require_gpu(o_latent, w_uv)
+    T, H, dc = o_latent.shape
+    if o_latent.dtype != torch.bfloat16 or dc != 512:
+        raise ValueError("o_latent must be bfloat16 [T, H, 512]")
+    if w_uv.dtype != torch.bfloat16 or tuple(w_uv.shape) != (H, 128, 512):
+        raise ValueError("w_uv must be bfloat16 [H, 128, 512]")
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=o_latent.device)
+    check(lib().mla_unabsorb_o(o_latent.data_ptr(), w_uv.data_ptr(), T, H, out.data_ptr(),
+                               _stream_handle(o_latent.device)))
+    return out
 

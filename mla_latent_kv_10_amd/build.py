@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["mla_abi.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_combine.hip", "mla_quantize.hip"]
+SOURCES = ["mla_abi.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_combine.hip", "mla_quantize.hip", "mla_absorb.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -9,6 +9,7 @@
 #include "mla.h"
 #include "mla_common.h"
 #include "mla_quantize.h"
+#include "mla_absorb.h"
 
 namespace {
 
@@ -230,6 +231,63 @@ int mla_quantize_fp8_append(const void* src, const int32_t* slots, int64_t n, vo
     p.num_rows = (int)(num_blocks * mla::kBlock);
     hipError_t e = mla::launch_quantize(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_absorb(int64_t tokens, int heads) {
+    if (tokens < 0) return fail(MLA_ERR_INVALID, "tokens must be >= 0 (got %lld)", (long long)tokens);
+    if (heads < 1) return fail(MLA_ERR_INVALID, "heads must be >= 1 (got %d)", heads);
+    if (heads > 4096) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 4096 (got %d)", heads);
+    if (tokens >= ((int64_t)1 << 31) / heads) return fail(MLA_ERR_UNSUPPORTED, "tokens * heads must be < 2^31");
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, int64_t tokens, int heads, void* q,
+                 void* stream) {
+    int st = check_absorb(tokens, heads);
+    if (st) return st;
+    if (tokens == 0) return ok();
+    if (!q_nope || !q_rope || !w_uk_t || !q) return fail(MLA_ERR_INVALID, "q_nope, q_rope, w_uk_t and q must be non-NULL");
+    if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk_t, 16) || !aligned(q, 16))
+        return fail(MLA_ERR_INVALID, "q_nope, q_rope, w_uk_t and q must be 16-byte aligned");
+    mla::AbsorbParams p;
+    p.x = static_cast<const uint16_t*>(q_nope);
+    p.w = static_cast<const uint16_t*>(w_uk_t);
+    p.rope = static_cast<const uint16_t*>(q_rope);
+    p.out = static_cast<uint16_t*>(q);
+    p.tokens = tokens;
+    p.heads = heads;
+    p.out_stride = mla::kDqk;
+    hipError_t e = mla::launch_absorb_q(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorb launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_unabsorb_o(const void* o_latent, const void* w_uv, int64_t tokens, int heads, void* out, void* stream) {
+    int st = check_absorb(tokens, heads);
+    if (st) return st;
+    if (tokens == 0) return ok();
+    if (!o_latent || !w_uv || !out) return fail(MLA_ERR_INVALID, "o_latent, w_uv and out must be non-NULL");
+    if (!aligned(o_latent, 16) || !aligned(w_uv, 16) || !aligned(out, 16))
+        return fail(MLA_ERR_INVALID, "o_latent, w_uv and out must be 16-byte aligned");
+    mla::AbsorbParams p;
+    p.x = static_cast<const uint16_t*>(o_latent);
+    p.w = static_cast<const uint16_t*>(w_uv);
+    p.rope = nullptr;
+    p.out = static_cast<uint16_t*>(out);
+    p.tokens = tokens;
+    p.heads = heads;
+    p.out_stride = 128;
+    hipError_t e = mla::launch_unabsorb_o(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "unabsorb launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -189,3 +189,33 @@ def test_quantize_rejects_bad_arguments(over, status, text):
 def test_quantize_with_no_rows_enqueues_nothing():
     # n == 0 returns before any HIP call, so it succeeds without a GPU and with NULL buffers
     assert m.lib().mla_quantize_fp8_append(0, 0, 0, 0, 4, None) == m.MLA_OK
+
+
+ABSORB_CASES = [
+    (dict(tokens=-1), m.MLA_ERR_INVALID, "tokens"),
+    (dict(heads=0), m.MLA_ERR_INVALID, "heads"),
+    (dict(heads=5000), m.MLA_ERR_UNSUPPORTED, "heads"),
+    (dict(tokens=1 << 31), m.MLA_ERR_UNSUPPORTED, "2^31"),
+    (dict(x=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(w=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(out=0), m.MLA_ERR_INVALID, "non-NULL"),
+    (dict(x=FAKE + 8), m.MLA_ERR_INVALID, "aligned"),
+    (dict(w=FAKE + 2), m.MLA_ERR_INVALID, "aligned"),
+    (dict(out=FAKE + 4), m.MLA_ERR_INVALID, "aligned"),
+]
+
+
+@pytest.mark.parametrize("over,status,text", ABSORB_CASES)
+def test_absorb_entry_points_reject_bad_arguments(over, status, text):
+    kw = dict(x=FAKE, w=FAKE, out=FAKE, tokens=8, heads=16)
+    kw.update(over)
+    L = m.lib()
+    assert L.mla_absorb_q(kw["x"], FAKE, kw["w"], kw["tokens"], kw["heads"], kw["out"], None) == status
+    assert text in L.mla_last_error().decode()
+    assert L.mla_unabsorb_o(kw["x"], kw["w"], kw["tokens"], kw["heads"], kw["out"], None) == status
+    assert text in L.mla_last_error().decode()
+
+
+def test_absorb_rope_pointer_is_checked():
+    assert m.lib().mla_absorb_q(FAKE, 0, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID
+    assert m.lib().mla_absorb_q(FAKE, FAKE + 8, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID

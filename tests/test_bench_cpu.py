@@ -57,3 +57,15 @@ def test_writer_traffic_row_and_cpu_leg():
     assert bench.measured_traffic(full, "-", "0" * 16, bench.QUANT_TRAFFIC_FILE) is None
     leg = bench.quantize_cpu_baseline(src, 0.2)
     assert leg["kind"] == "oracle" and leg["unit"] == "GB/s" and leg["value"] > 0
+
+
+def test_absorb_counts_and_traffic_rows():
+    ba, bu, flops = bench.absorb_counts(128, 128)
+    w = 128 * 128 * 512 * 2
+    assert ba == w + 128 * 128 * (128 + 64 + 576) * 2 and bu == w + 128 * 128 * (512 + 128) * 2
+    assert flops == 2 * 128 * 128 * 128 * 512
+    name = "absorption products: T=128 tokens (B=64 x s_q=2), H=128"
+    h = bench.source_hash(bench.ABSORB_SOURCES, "mla_absorb.hip")
+    for kern, algo in (("absorb_q", ba), ("unabsorb_o", bu)):
+        got = bench.measured_traffic(name, kern, h, bench.ABSORB_TRAFFIC_FILE)
+        assert got is not None and algo <= got < 1.05 * algo

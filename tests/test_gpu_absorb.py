@@ -1,0 +1,133 @@
+"""Absorption products on the GPU (mla_absorb_q, mla_unabsorb_o through the C ABI)
+against the oracle, and the whole absorbed layer (absorb, decode, unabsorb).
+
+Tolerance, from the arithmetic: each output is an fp32 sum of K exact bf16
+products rounded once to bf16, so |gpu - ref| <= 2^-8 |ref| (bf16 rounding)
++ K 2^-24 sum_k |x_k w_k| (fp32 summation in any order). The RoPE part of the
+absorbed query is a copy: bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_10_amd as mla
+from oracle import mla_decode_ref
+from oracle.absorb import absorb_q, unabsorb_o
+
+from tests.gpu_helpers import compare, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _bits(x: torch.Tensor) -> np.ndarray:
+    return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _vals(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _bound(x_bits, w_bits, ref, K, transpose_w):
+    """2^-8 |ref| + K 2^-24 sum_k |x_k w_k| per output."""
+    ax, aw = np.abs(_vals(x_bits)), np.abs(_vals(w_bits))
+    T, H = ax.shape[:2]
+    S = np.empty_like(ref)
+    for h in range(H):
+        S[:, h] = ax[:, h] @ (aw[h] if transpose_w else aw[h].T)
+    return 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -24 * S * 1.01 + 1e-30
+
+
+def _inputs(T, H, seed):
+    g = torch.Generator().manual_seed(seed)
+    q_nope = torch.randn(T, H, 128, generator=g).to(torch.bfloat16)
+    q_rope = torch.randn(T, H, 64, generator=g).to(torch.bfloat16)
+    w_uk = (torch.randn(H, 128, 512, generator=g) / 512 ** 0.5).to(torch.bfloat16)
+    w_uv = (torch.randn(H, 128, 512, generator=g) / 512 ** 0.5).to(torch.bfloat16)
+    o_lat = torch.randn(T, H, 512, generator=g).to(torch.bfloat16)
+    return q_nope, q_rope, w_uk, w_uv, o_lat
+
+
+SHAPES = [(1, 1), (16, 128), (128, 128), (37, 12), (33, 16), (65, 8)]
+
+
+@pytest.mark.parametrize("T,H", SHAPES)
+def test_absorb_q_matches_oracle(T, H):
+    say(f"absorb_q T={T} H={H}")
+    q_nope, q_rope, w_uk, _, _ = _inputs(T, H, T * 1000 + H)
+    w_uk_t = w_uk.transpose(1, 2).contiguous()                      # [H, 512, 128]
+    got = mla.absorb_q(q_nope.to(DEV), q_rope.to(DEV), w_uk_t.to(DEV))
+    torch.cuda.synchronize()
+    ref = absorb_q(_bits(q_nope), _bits(q_rope), _bits(w_uk))
+    g = got.float().cpu().numpy().astype(np.float64)
+    bound = _bound(_bits(q_nope), _bits(w_uk), ref[:, :, :512], 128, transpose_w=True)
+    assert np.all(np.abs(g[:, :, :512] - ref[:, :, :512]) <= bound)
+    assert np.array_equal(_bits(got.cpu())[:, :, 512:], _bits(q_rope))
+
+
+@pytest.mark.parametrize("T,H", SHAPES)
+def test_unabsorb_o_matches_oracle(T, H):
+    say(f"unabsorb_o T={T} H={H}")
+    _, _, _, w_uv, o_lat = _inputs(T, H, T * 1000 + H + 1)
+    got = mla.unabsorb_o(o_lat.to(DEV), w_uv.to(DEV))
+    torch.cuda.synchronize()
+    ref = unabsorb_o(_bits(o_lat), _bits(w_uv))
+    bound = _bound(_bits(o_lat), _bits(w_uv), ref, 512, transpose_w=False)
+    assert np.all(np.abs(got.float().cpu().numpy() - ref) <= bound)
+
+
+def test_empty_calls_write_nothing():
+    say("absorb: tokens = 0")
+    out = torch.full((4,), 3, dtype=torch.int32, device=DEV)
+    L = mla.lib()
+    assert L.mla_absorb_q(0, 0, 0, 0, 8, out.data_ptr(), None) == 0
+    assert L.mla_unabsorb_o(0, 0, 0, 8, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert bool((out == 3).all())
+
+
+def test_absorbed_layer_end_to_end():
+    # absorb -> dense bf16 decode -> unabsorb on the GPU, each stage held to its own bar on the stage's GPU input
+    B, s_q, H = 4, 2, 128
+    lens = [200, 64, 1, 333]
+    say("absorbed layer: absorb, decode, unabsorb")
+    g = torch.Generator().manual_seed(9)
+    T = B * s_q
+    q_nope = torch.randn(T, H, 128, generator=g).to(torch.bfloat16)
+    q_rope = torch.randn(T, H, 64, generator=g).to(torch.bfloat16)
+    w_uk = (torch.randn(H, 128, 512, generator=g) / 512 ** 0.5).to(torch.bfloat16)
+    w_uv = (torch.randn(H, 128, 512, generator=g) / 512 ** 0.5).to(torch.bfloat16)
+    n_blocks = sum((L + 63) // 64 for L in lens)
+    mbps = max((L + 63) // 64 for L in lens)
+    kv = torch.randn(n_blocks, 64, 576, generator=g).to(torch.bfloat16)
+    perm = torch.randperm(n_blocks, generator=g).to(torch.int32)
+    bt = torch.full((B, mbps), -1, dtype=torch.int32)
+    p = 0
+    for b, L in enumerate(lens):
+        nb = (L + 63) // 64
+        bt[b, :nb] = perm[p:p + nb]
+        p += nb
+    seq = torch.tensor(lens, dtype=torch.int32)
+    scale = float(np.float32(576 ** -0.5))
+
+    q = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=DEV)
+    mla.absorb_q(q_nope.to(DEV), q_rope.to(DEV), w_uk.transpose(1, 2).contiguous().to(DEV), out=q)
+    tm, so = mla.get_mla_metadata(seq.to(DEV), s_q, H)
+    o, lse = mla.mla_decode_with_kvcache(q, kv.to(DEV), bt.to(DEV), seq.to(DEV), 512, tm, so, softmax_scale=scale,
+                                         causal=True)
+    out = mla.unabsorb_o(o.view(T, H, 512), w_uv.to(DEV))
+    torch.cuda.synchronize()
+
+    q_ref = absorb_q(_bits(q_nope), _bits(q_rope), _bits(w_uk))
+    q_bits = _bits(q.cpu()).reshape(T, H, 576)
+    bound = _bound(_bits(q_nope), _bits(w_uk), q_ref[:, :, :512], 128, transpose_w=True)
+    assert np.all(np.abs(_vals(q_bits)[:, :, :512] - q_ref[:, :, :512]) <= bound)
+    o_ref, lse_ref = mla_decode_ref(q_bits.reshape(B, s_q, H, 576), _bits(kv).reshape(n_blocks, 64, 576).view(np.uint8)
+                                    .reshape(n_blocks, 64, 1152), "bf16", block_table=bt.numpy(),
+                                    cache_seqlens=seq.numpy(), softmax_scale=scale, causal=True)
+    compare(o, lse, o_ref, lse_ref, label="decode on the absorbed q")  # includes the empty row (L = 1, query 0)
+    o_bits = _bits(o.cpu()).reshape(T, H, 512)
+    u_ref = unabsorb_o(o_bits, _bits(w_uv))
+    assert np.all(np.abs(out.float().cpu().numpy() - u_ref) <= _bound(o_bits, _bits(w_uv), u_ref, 512, False))
