@@ -365,7 +365,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: dense bf16 h_q=128)")
+    ap.add_argument("--config", type=int, default=2, help="workload 1..6 (default 2: dense bf16 h_q=128; 6: sparse prefill)")
     ap.add_argument("--seqlen", type=int, default=65536, help="sequence length for workload 3")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

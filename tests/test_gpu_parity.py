@@ -1,6 +1,6 @@
 """HIP decode vs the float64 oracle on the same seeded inputs.
 
-Small cases are compared on every query row; the five full-size workloads are
+Small cases are compared on every query row; the six full-size workloads are
 compared on sampled (b, i) rows that the oracle computes one by one, in the
 launch configuration the benchmark uses (metadata with the default number of
 parts, decode + combine)."""
@@ -56,6 +56,10 @@ SMALL = [
                               invalid_frac=0.05)),
     ("bf16 sparse h4 mostly invalid", dict(batch=2, s_q=1, h_q=4, kv_format="bf16", topk=100,
                                            sparse_tokens_per_seq=256, invalid_frac=0.95)),
+    ("bf16 sparse prefill chunk h128 s_q=40", dict(batch=2, s_q=40, h_q=128, kv_format="bf16", topk=192,
+                                                   sparse_tokens_per_seq=512, prefix_sparse=True)),
+    ("fp8 sparse prefill chunk h16 s_q=33", dict(batch=1, s_q=33, h_q=16, kv_format="fp8", topk=100,
+                                                 sparse_tokens_per_seq=256, prefix_sparse=True, invalid_frac=0.1)),
 ]
 
 
@@ -104,3 +108,9 @@ def test_config4_fp8_causal_sampled():
 def test_config5_sparse_fp8_sampled():
     w = config_workload(5)
     _check(w, rows=[(0, 0), (9, 0), (31, 0)], label="config 5 (sparse fp8, sampled rows)")
+
+
+def test_config6_sparse_prefill_sampled():
+    w = config_workload(6)
+    _check(w, rows=[(0, 0), (0, 511), (0, 1023)], label="config 6 (sparse prefill, sampled rows)")
+

@@ -50,3 +50,16 @@ def test_config5_recipe():
     w = config_workload(5)
     assert tuple(w.kv.shape) == (16384, 64, 656)
     assert torch.all((w.indices == -1).sum(dim=2) == 102)
+
+
+def test_sparse_prefill_recipe():
+    w = config_workload(6)
+    assert w.q.shape == (1, 1024, 128, 576) and w.kv.shape == (512, 64, 1152) and w.indices.shape == (1, 1024, 2048)
+    idx = w.indices.numpy()[0]
+    T, s_q = 32768, 1024
+    for i in (0, 1, 500, 1023):
+        row = idx[i]
+        assert row.min() >= 0 and row.max() <= T - s_q + i   # inside query i's visible prefix
+        assert len(np.unique(row)) == row.size               # distinct
+    assert not w.causal and w.block_table is None
+

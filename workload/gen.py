@@ -41,6 +41,7 @@ CONFIG_NAMES = {
     3: "low-head dense bf16: B=16 s_q=1 h_q=16 L fixed",
     4: "fp8 paged causal: B=64 s_q=2 h_q=128 L=8192",
     5: "sparse fp8: B=32 s_q=1 h_q=128 topk=2048 (5% -1)",
+    6: "sparse prefill bf16: B=1 s_q=1024 h_q=128 topk=2048 over a 32768-token prefix",
 }
 
 
@@ -143,6 +144,7 @@ def make_workload(
     topk: int = 0,
     sparse_tokens_per_seq: int = 0,
     invalid_frac: float = 0.0,
+    prefix_sparse: bool = False,
     shuffle_pages: bool = True,
     extra_blocks: int = 0,
     softmax_scale: Optional[float] = None,
@@ -160,7 +162,9 @@ def make_workload(
     [b*T, (b+1)*T) with T = sparse_tokens_per_seq; indices[b, i, :] are topk
     distinct rows of that range in random order; round(invalid_frac * topk)
     positions per (b, i) are set to -1. block_table is None and cache_seqlens
-    holds T.
+    holds T. With prefix_sparse (a prefill chunk: the s_q queries are the
+    sequence's last s_q tokens), query i at position T - s_q + i draws its
+    topk rows from its own visible prefix [0, T - s_q + i] instead.
     """
     gen = torch.Generator().manual_seed(seed)
     if softmax_scale is None:
@@ -196,7 +200,9 @@ def make_workload(
     idx = torch.empty((batch, s_q, topk), dtype=torch.int32)
     for b in range(batch):
         for i in range(s_q):
-            idx[b, i] = (torch.randperm(T, generator=gen)[:topk] + b * T).to(torch.int32)
+            visible = T - s_q + i + 1 if prefix_sparse else T
+            assert visible >= topk
+            idx[b, i] = (torch.randperm(visible, generator=gen)[:topk] + b * T).to(torch.int32)
     n_inv = int(round(invalid_frac * topk))
     if n_inv:
         for b in range(batch):
@@ -209,7 +215,7 @@ def make_workload(
 
 
 def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
-    """The five decode workloads (config 3 takes its fixed sequence length)."""
+    """The five decode workloads and the sparse prefill chunk (config 3 takes its fixed sequence length)."""
     if cfg == 1:
         # q and cache drawn in fp32 then rounded to bf16; 4 pages, shuffled.
         return make_workload(batch=1, s_q=1, h_q=4, seqlens=[256], kv_format="bf16",
@@ -227,4 +233,7 @@ def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
         return make_workload(batch=32, s_q=1, h_q=128, kv_format="fp8", topk=2048,
                              sparse_tokens_per_seq=32768, invalid_frac=0.05, seed=seed,
                              name=CONFIG_NAMES[5])
+    if cfg == 6:
+        return make_workload(batch=1, s_q=1024, h_q=128, kv_format="bf16", topk=2048,
+                             sparse_tokens_per_seq=32768, prefix_sparse=True, seed=seed, name=CONFIG_NAMES[6])
     raise ValueError(f"unknown config {cfg}")
