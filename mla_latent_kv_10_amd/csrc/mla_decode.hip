@@ -55,9 +55,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // other variants use one array (the 64- and 16-head ones reuse all of it
     // for their end-of-segment merge).
     constexpr bool kFp8Pipe = FP8 && VAR == kV128;
-    // Dense bf16 with 128-head groups issues each tile's loads between the
-    // score MFMAs of the tile before it (see the tile pipeline).
-    constexpr bool kQkLoads = !FP8 && !SPARSE && VAR == kV128;
+    // bf16 with 128-head groups (dense or sparse) issues each tile's loads
+    // between the score MFMAs of the tile before it (see the tile pipeline).
+    constexpr bool kQkLoads = !FP8 && VAR == kV128;
     // Every dense variant reads block-table words as scalar loads and issues
     // its tile loads as inline asm the compiler does not track, so that no
     // compiler wait for a load in flight lands inside the tile loop (in the
@@ -721,9 +721,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const int g = j / 9, ug = j % 9;
                 dma16_asm(kv_words, lds_addr(dst + (((2 * wave + g) * 9 + ug) << 10)), rows[g], (unsigned)uu16[g], ug * 128);
             };
+            // each chunk's cache row: dense -> from the page; sparse -> the
+            // index entry of the chunk's token, held by the lane of that token
             auto tile_rows = [&](const TileSrc& tsrc, unsigned (&rows)[2]) {
                 #pragma unroll
-                for (int g = 0; g < 2; ++g) rows[g] = dense_row(tsrc.page0, tsrc.n_valid, trow[g]);
+                for (int g = 0; g < 2; ++g) {
+                    if constexpr (SPARSE) rows[g] = (unsigned)__shfl((int)tsrc.srow, trow[g], 64);
+                    else rows[g] = dense_row(tsrc.page0, tsrc.n_valid, trow[g]);
+                }
             };
             TileSrc ts = tile_src(t0, idx_a);
             uint64_t mask_a = ts.mask;
@@ -738,9 +743,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             for (int k = t0; k <= t1; ++k) {
                 char LDS_AS* cur = ((k - t0) & 1) ? buf1 : buf0;
                 char LDS_AS* nxt = ((k - t0) & 1) ? buf0 : buf1;
-                const unsigned idx_f = fetch_index(k + 2);
-                wait_vm(0);        // tile k's loads are the only VMEM in flight
+                // index word of tile k + 2: dense -> a scalar load, issued early;
+                // sparse -> a VMEM load, issued after the wait below so that the
+                // wait never includes it (it has a whole tile to land)
+                unsigned idx_f = kOOB;
+                if constexpr (!SPARSE) idx_f = fetch_index(k + 2);
+                wait_vm(0);        // tile k's loads (and a sparse index word) are all the VMEM in flight
                 block_sync_lds();  // ... and every wave is done with nxt (tile k - 1)
+                if constexpr (SPARSE) idx_f = fetch_index(k + 2);
                 const TileSrc tn = (k + 1 <= t1) ? tile_src(k + 1, idx_n) : none;
                 unsigned rows[2];
                 tile_rows(tn, rows);
