@@ -63,7 +63,7 @@ extern "C" {
  *   non-empty one first taking FIXED_COST positions, then one per tile; with
  *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
  *   MIN_PAYLOAD), the tile at position x goes to work part floor(x / W).
- *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 4; RG 64 -> 2 and 2;
+ *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 3; RG 64 -> 2 and 2;
  *   RG 16 -> 0 and 1.
  *   Placement: when num_parts is a multiple of 8, with used = ceil(total / W)
  *   and k = ceil(used / 8), work part j is row (j / k) * (num_parts / 8) +
@@ -87,12 +87,16 @@ int mla_metadata_size(int batch, int s_q, int h_q, int num_parts,
                       int64_t* tile_meta_elems, int64_t* split_offsets_elems);
 
 /*
- * Bytes of fp32 split workspace mla_decode_with_kvcache needs. Layout, with
- * S = Q + num_parts slots: partial outputs, S slots of RG x 512 fp32 (each
- * already divided by its own softmax sum), then, at the next 256-byte
- * boundary, partial lse fp32 [S][RG]. Inside a slot, RG = 16 is row-major
- * [row][512]; RG = 128 and 64 are blocked as the split kernel's registers hold it:
- * the float4 at index ((w * 16 + dd) * 4 + g) * 64 + lane holds row
+ * Bytes of split workspace mla_decode_with_kvcache needs. Layout, with
+ * S = Q + num_parts slots: partial outputs, S slots of RG x 512 fp16; then, at
+ * the next 256-byte boundary, partial lse fp32 [S][RG]; then partial scales
+ * fp32 [S][RG]. A partial row o_k (already divided by its own softmax sum) is
+ * stored as fp16(o_k / c), c = its scale, a power of two chosen so that the
+ * row's largest |o_k / c| lies in [2^14, 2^15) (c = 1 for an all-zero row):
+ * 11 significant bits over the row's own range, far below the bf16 rounding
+ * of the final o. Inside a slot, RG = 16 is row-major [row][512]; RG = 128
+ * and 64 are blocked as the split kernel's registers hold it: the group of 4
+ * values at index ((w * 16 + dd) * 4 + g) * 64 + lane holds row
  * 32 w + (lane & 31), dims 32 dd + 8 g + 4 (lane >> 5) + 0..3. The slots of
  * row-group sequence q are split_offsets[q] .. split_offsets[q + 1] - 1, in
  * KV order.
@@ -167,7 +171,7 @@ int mla_decode_with_kvcache(const mla_decode_args* args, void* stream);
 /*
  * The split kernel of mla_decode_with_kvcache alone: each part attends its
  * tile ranges ([Walkthrough] §七, split-KV). Rows of a sequence with a
- * single split are finished (o, lse); the others leave fp32 partials in the
+ * single split are finished (o, lse); the others leave partials in the
  * workspace for mla_combine, which must follow on the same stream with the
  * same arguments before o and lse are read. Lets a caller place work between
  * the two kernels. Same arguments and errors as mla_decode_with_kvcache.

@@ -47,9 +47,9 @@ int check_shape(int batch, int s_q, int h_q, int num_parts) {
 size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
     const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
     const size_t slots = (size_t)batch * l.n_rg + (size_t)num_parts;
-    const size_t o_bytes = slots * l.rg * mla::kDv * sizeof(float);
+    const size_t o_bytes = slots * l.rg * mla::kDv * sizeof(uint16_t);
     const size_t lse_bytes = slots * l.rg * sizeof(float);
-    return ((o_bytes + 255) & ~(size_t)255) + lse_bytes;
+    return ((o_bytes + 255) & ~(size_t)255) + 2 * lse_bytes;
 }
 
 // Validates a decode call; fills the kernel parameters.
@@ -93,7 +93,7 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
 
     const mla::Layout l = mla::layout_for(a->h_q, a->s_q, a->batch, a->num_parts);
     const size_t slots = (size_t)a->batch * l.n_rg + (size_t)a->num_parts;
-    const size_t o_bytes = ((slots * l.rg * mla::kDv * sizeof(float)) + 255) & ~(size_t)255;
+    const size_t o_bytes = ((slots * l.rg * mla::kDv * sizeof(uint16_t)) + 255) & ~(size_t)255;
     p->q = static_cast<const uint16_t*>(a->q);
     p->kv = static_cast<const uint8_t*>(a->kv);
     p->block_table = a->block_table;
@@ -101,8 +101,9 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     p->indices = a->indices;
     p->tile_meta = a->tile_meta;
     p->split_offsets = a->split_offsets;
-    p->ws_o = static_cast<float*>(a->workspace);
+    p->ws_o = static_cast<uint16_t*>(a->workspace);
     p->ws_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + o_bytes);
+    p->ws_scale = p->ws_lse + slots * l.rg;
     p->o = static_cast<uint16_t*>(a->o);
     p->lse = a->lse;
     p->batch = a->batch;

@@ -8,13 +8,14 @@
 // (lse_k = -inf) weigh zero; a row with no partial at all gets o = 0 and
 // lse = -inf; a row with exactly one split was written by the split kernel.
 //
-// Workspace layout of one slot (RG rows x 512 dims, fp32):
-//   RG = 128 or 64: blocked as the split kernel's MFMA registers hold it, float4
-//     index ((w * 16 + dd) * 4 + g) * 64 + lane for row 32 w + (lane & 31),
+// Workspace layout of one slot (RG rows x 512 dims, fp16 values o_k / c_k,
+// where c_k, a power of two per slot and row, sits in ws_scale):
+//   RG = 128 or 64: blocked as the split kernel's MFMA registers hold it, 4-value
+//     group index ((w * 16 + dd) * 4 + g) * 64 + lane for row 32 w + (lane & 31),
 //     dims 32 dd + 8 g + 4 (lane >> 5) + 0..3;
 //   RG = 16: row-major [row][512].
-// Each thread owns one row and a fixed set of float4s; consecutive threads
-// read consecutive float4s of a slot.
+// Each thread owns one row and a fixed set of 4-value groups; consecutive
+// threads read consecutive groups of a slot.
 #include <type_traits>
 
 #include "mla_common.h"
@@ -24,13 +25,15 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 template <int RG>
 struct CombineMap {
-    // blocks per row-group sequence, float4s per thread per slot
+    // blocks per row-group sequence, 4-value groups per thread per slot
     static constexpr int kBlocksPerQ = RG == 16 ? 4 : RG / 4;  // 128 -> 32, 64 -> 16
     static constexpr int kVec = 2;
-    // thread -> (row, float4 offsets within the slot, dims of each float4)
+    // thread -> (row, group offsets within the slot, dims of each group)
     __device__ static void map(int blk, int t, int& row, int (&f4)[kVec], int (&dim)[kVec]) {
         if constexpr (RG != 16) {
             const int w = blk >> 3, dq = blk & 7;
@@ -56,10 +59,10 @@ struct CombineMap {
 };
 
 // One pass over the splits, kU at a time: every load of a chunk (its lse
-// values and its partial rows) is issued before any of them is used, and the
-// running reference m moves with a rescale of the sums, as in the online
-// softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} o_k / s with
-// s = sum_k e^{lse_k - m}, lse = m + ln s.
+// values, scales and partial rows) is issued before any of them is used, and
+// the running reference m moves with a rescale of the sums, as in the online
+// softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} c_k h_k / s
+// with h_k the stored fp16 row, s = sum_k e^{lse_k - m}, lse = m + ln s.
 template <int RG>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     using M = CombineMap<RG>;
@@ -81,11 +84,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     if (n == 1) return;  // the split kernel wrote the final row
     const int64_t orow = ((int64_t)b * p.s_q + i) * p.h_q + h;
     uint16_t* op = p.o + orow * kDv;
-    const float* lse_k = p.ws_lse + (int64_t)s0 * RG + row;
     const bool lse_writer = dim[0] == 0;  // exactly one thread per row holds dim 0
-    const f32x4* base = (const f32x4*)(p.ws_o + (int64_t)s0 * RG * kDv);
-    constexpr int kSlot4 = RG * kDv / 4;  // float4s per slot
-    constexpr int kU = 16;                // splits in flight
+    constexpr int kSlotBytes = RG * kDv * 2;  // fp16 partial rows of one slot
     float m = -INFINITY, s = 0.f;
     f32x4 acc[M::kVec];
     #pragma unroll
@@ -93,26 +93,43 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     // Each partial is read exactly once. With three or more splits the loads
     // are non-temporal (measured faster); with two (long sequences, many
     // workgroups) the default policy measured faster.
-    auto merge = [&](auto nt_tag) {
-        constexpr bool NT = decltype(nt_tag)::value;
+    // kU splits in flight per chunk: the power of two in 2..16 nearest above n,
+    // so a sequence with few splits issues few loads.
+    auto merge = [&](auto nt_tag, auto ku_tag) {
+        constexpr int AUX = decltype(nt_tag)::value ? 2 : 0;  // 2: nt
+        constexpr int kU = decltype(ku_tag)::value;
         for (int k0 = 0; k0 < n; k0 += kU) {
-            float lv[kU];
-            f32x4 v[kU][M::kVec];
+            // Buffer descriptors over this chunk's splits only: a load past the
+            // last split returns 0 without touching memory, so all kU loads
+            // issue unconditionally (a conditional load would become a branch
+            // closed by a wait, one round trip per split).
+            const int nc = min(kU, n - k0);
+            const int64_t slot0 = (int64_t)s0 + k0;
+            const __amdgpu_buffer_rsrc_t o_rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(p.ws_o + slot0 * RG * kDv), (short)0, nc * kSlotBytes, 0x00020000);
+            const __amdgpu_buffer_rsrc_t l_rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(p.ws_lse + slot0 * RG), (short)0, nc * RG * 4, 0x00020000);
+            const __amdgpu_buffer_rsrc_t c_rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(p.ws_scale + slot0 * RG), (short)0, nc * RG * 4, 0x00020000);
+            float lv[kU], cv[kU];
+            u32x2 v[kU][M::kVec];
             #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const bool in = k0 + u < n;
-                lv[u] = in ? lse_k[(int64_t)(k0 + u) * RG] : -INFINITY;
+                lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, (u * RG + row) * 4, 0, 0));
+                cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c_rs, (u * RG + row) * 4, 0, 0));
                 #pragma unroll
-                for (int j = 0; j < M::kVec; ++j) {
-                    const f32x4* src = &base[(int64_t)(k0 + u) * kSlot4 + f4[j]];
-                    if constexpr (NT) v[u][j] = in ? __builtin_nontemporal_load(src) : f32x4{0.f, 0.f, 0.f, 0.f};
-                    else v[u][j] = in ? *src : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int j = 0; j < M::kVec; ++j)
+                    v[u][j] = __builtin_amdgcn_raw_buffer_load_b64(o_rs, u * kSlotBytes + f4[j] * 8, 0, AUX);
             }
+            #pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (u >= nc) lv[u] = -INFINITY;
             float mc = m;
             #pragma unroll
             for (int u = 0; u < kU; ++u) mc = fmaxf(mc, lv[u]);
-            if (mc == -INFINITY) continue;  // nothing attended so far
+            // Branch-free (a branch here would let the compiler sink the data
+            // loads below it, a second round trip): while nothing is attended
+            // (mc = -inf) every weight is 0 and the sums stay 0.
             const float r = (m == -INFINITY) ? 0.f : __expf(m - mc);
             s *= r;
             #pragma unroll
@@ -121,14 +138,22 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
             for (int u = 0; u < kU; ++u) {
                 const float wgt = lv[u] == -INFINITY ? 0.f : __expf(lv[u] - mc);
                 s += wgt;
+                const float wc = wgt * cv[u];
                 #pragma unroll
-                for (int j = 0; j < M::kVec; ++j) acc[j] += wgt * v[u][j];
+                for (int j = 0; j < M::kVec; ++j)
+                    acc[j] += wc * __builtin_convertvector(__builtin_bit_cast(f16x4, v[u][j]), f32x4);
             }
             m = mc;
         }
     };
-    if (n >= 3) merge(std::true_type{});
-    else merge(std::false_type{});
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    using I16 = std::integral_constant<int, 16>;
+    if (n <= 2) merge(std::false_type{}, I2{});
+    else if (n <= 4) merge(std::true_type{}, I4{});
+    else if (n <= 8) merge(std::true_type{}, I8{});
+    else merge(std::true_type{}, I16{});
     // no split attended anything (or no split at all): o = 0, lse = -inf
     const bool empty = m == -INFINITY;
     const float inv = empty ? 0.f : 1.f / s;

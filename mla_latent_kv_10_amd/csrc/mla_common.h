@@ -46,7 +46,7 @@ inline Layout layout_for(int h_q, int s_q, int batch, int num_parts) {
     } else if (h_q <= 64) {
         l.rg = 64; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV64;
     } else {
-        l.rg = 128; l.fixed_cost = 2; l.min_payload = 4; l.variant = kV128;
+        l.rg = 128; l.fixed_cost = 2; l.min_payload = 3; l.variant = kV128;
     }
     l.n_hb = (h_q + l.rg - 1) / l.rg;
     l.n_rg = s_q * l.n_hb;
@@ -68,8 +68,9 @@ struct DecodeParams {
     const int32_t* indices;     // [B, s_q, topk]
     const int32_t* tile_meta;   // [num_parts, 8]
     const int32_t* split_offsets;
-    float* ws_o;                // [slots, rg, 512]
+    uint16_t* ws_o;             // fp16 bits [slots, rg, 512]: partial o times 1 / ws_scale
     float* ws_lse;              // [slots, rg]
+    float* ws_scale;            // [slots, rg]: power of two the stored partial row is scaled by
     uint16_t* o;                // bf16 bits [B, s_q, h_q, 512]
     float* lse;                 // [B, s_q, h_q]
     int batch, s_q, h_q, n_hb, n_rg, rg, mbps, topk, causal, num_rows, num_parts, row_bytes;

@@ -867,17 +867,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if (hh == 0) p.lse[qrow0 + h] = lse_v;
                 }
             } else {
-                // blocked partial layout: one 1 KB contiguous store per (d, g) per wave
-                f32x4* wp = (f32x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + lane;
+                // fp16 partial o * 2^-e, e from the row's largest |o| (its two
+                // lanes hold 256 dims each). Blocked layout: one 512-byte
+                // contiguous store per (d, g) per wave.
+                float amax = 0.f;
+                #pragma unroll
+                for (int d = 0; d < 16; ++d)
+                    #pragma unroll
+                    for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(oacc[d][v]));
+                amax = fmaxf(amax, wave_shfl_xor(amax, 32));
+                const unsigned ef = partial_exp_field(amax * inv);
+                const float sc = inv * exp_field_inv_pow2(ef);  // exact: inv times a power of two
+                f16x4* wp = (f16x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + lane;
                 #pragma unroll
                 for (int d = 0; d < 16; ++d) {
                     #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        f32x4 w = {oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv, oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv};
-                        wp[(d * 4 + g) * 64] = w;
-                    }
+                    for (int g = 0; g < 4; ++g)
+                        wp[(d * 4 + g) * 64] = to_f16x4(oacc[d][4 * g] * sc, oacc[d][4 * g + 1] * sc,
+                                                        oacc[d][4 * g + 2] * sc, oacc[d][4 * g + 3] * sc);
                 }
-                if (hh == 0) p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
+                if (hh == 0) {
+                    p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
+                    p.ws_scale[(int64_t)sg.slot * RG + rloc] = exp_field_pow2(ef);
+                }
             }
           }
         } else {
@@ -927,10 +939,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if ((tid & 15) == 0) p.lse[qrow0 + h] = lse_v;
                 }
             } else {
-                float* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + c4;
+                // fp16 partial o * 2^-e, e from the row's largest |o| (16 lanes
+                // hold its 512 dims)
+                float amax = 0.f;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) *(f32x4*)(wp + 64 * j) = acc[j];
-                if ((tid & 15) == 0) p.ws_lse[(int64_t)sg.slot * RG + mr] = lse_v;
+                for (int j = 0; j < 8; ++j)
+                    #pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) amax = fmaxf(amax, fabsf(acc[j][e2]));
+                #pragma unroll
+                for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
+                const unsigned ef = partial_exp_field(amax);
+                const float sc = exp_field_inv_pow2(ef);
+                uint16_t* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + c4;
+                #pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *(f16x4*)(wp + 64 * j) = to_f16x4(acc[j][0] * sc, acc[j][1] * sc, acc[j][2] * sc, acc[j][3] * sc);
+                if ((tid & 15) == 0) {
+                    p.ws_lse[(int64_t)sg.slot * RG + mr] = lse_v;
+                    p.ws_scale[(int64_t)sg.slot * RG + mr] = exp_field_pow2(ef);
+                }
             }
             block_sync_lds();  // merge buffers are read before the next segment's DMA
         }

@@ -199,6 +199,28 @@ __device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const 
 // >= 24 wait states: covers XDL-result -> VALU/accvgpr-read and VALU-write -> XDL-read hazards.
 __device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// ---------------------------------------------------------------- split partials
+
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+// Split partials are stored as fp16 of o_k * 2^-e, with 2^-e chosen from the
+// row's largest |o_k| (amax) so that it lands in [2^14, 2^15): fp16 keeps 11
+// significant bits over that row's range, and the power of two makes the
+// scaling itself exact. Returns the biased fp32 exponent field of 2^e
+// (2^e = 1 for amax = 0; e never below -126).
+__device__ __forceinline__ unsigned partial_exp_field(float amax) {
+    if (!(amax > 0.f)) return 127u;
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 14;  // amax < 2^(field - 126)
+    return (unsigned)max(e, 1);
+}
+// 2^e and 2^-e from that field (both normal floats: field in [1, 241])
+__device__ __forceinline__ float exp_field_pow2(unsigned f) { return __uint_as_float(f << 23); }
+__device__ __forceinline__ float exp_field_inv_pow2(unsigned f) { return __uint_as_float((254u - f) << 23); }
+
+__device__ __forceinline__ f16x4 to_f16x4(float a, float b, float c, float d) {
+    return f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
 // ---------------------------------------------------------------- segment context
 
 struct Seg {

@@ -63,12 +63,13 @@ def test_sizes():
     assert m.metadata_size(16, 1, 16, 256) == (256 * 8, 17)
     # 16 < h_q <= 64: 64-head groups
     assert m.metadata_size(16, 1, 40, 256) == (256 * 8, 16 + 1)
+    # fp16 partial rows, then fp32 lse and fp32 scale per (slot, row)
     ws = m.workspace_size(16, 1, 64, 256)
     slots = 16 + 256
-    assert ws == ((slots * 64 * 512 * 4 + 255) // 256) * 256 + slots * 64 * 4
+    assert ws == ((slots * 64 * 512 * 2 + 255) // 256) * 256 + 2 * slots * 64 * 4
     ws = m.workspace_size(64, 1, 128, 256)
     slots = 64 + 256
-    assert ws == ((slots * 128 * 512 * 4 + 255) // 256) * 256 + slots * 128 * 4
+    assert ws == ((slots * 128 * 512 * 2 + 255) // 256) * 256 + 2 * slots * 128 * 4
 
 
 @pytest.mark.parametrize("bad", [dict(batch=0), dict(s_q=0), dict(h_q=0), dict(num_parts=0), dict(num_parts=70000)])

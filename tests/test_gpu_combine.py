@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 def _slot_layout(part_o):
     """Logical partials [S][RG][512] -> the documented workspace layout
-    (RG = 16 row-major; RG = 128 or 64 blocked: float4 ((w*16+dd)*4+g)*64+lane
-    holds row 32w+(lane&31), dims 32dd+8g+4(lane>>5)+0..3)."""
+    (RG = 16 row-major; RG = 128 or 64 blocked: 4-value group
+    ((w*16+dd)*4+g)*64+lane holds row 32w+(lane&31), dims 32dd+8g+4(lane>>5)+0..3)."""
     S, RG, _ = part_o.shape
     if RG == 16:
         return np.ascontiguousarray(part_o)
@@ -33,17 +33,20 @@ def _slot_layout(part_o):
     return out.reshape(S, RG, 512)
 
 
-@pytest.mark.parametrize("h_q,s_q,P", [(128, 1, 8), (64, 1, 64), (16, 2, 8), (20, 1, 8), (100, 2, 8)])
-def test_combine_matches_oracle_merge(h_q, s_q, P):
-    say(f"combine h_q={h_q} s_q={s_q} parts={P}")
+@pytest.mark.parametrize("B,h_q,s_q,P,max_splits", [(3, 128, 1, 8, 5), (3, 64, 1, 64, 5), (3, 16, 2, 8, 5),
+                                                   (3, 20, 1, 8, 5), (3, 100, 2, 8, 5), (10, 128, 1, 200, 40),
+                                                   (10, 16, 1, 200, 40), (6, 64, 2, 240, 40)])
+def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
+    """Split counts 0..max_splits-1: every chunk size of the merge (2, 4, 8, 16
+    splits in flight) and sequences spanning several chunks."""
+    say(f"combine h_q={h_q} s_q={s_q} parts={P} splits<{max_splits}")
     dev = "cuda:0"
-    B = 3
     RG = 16 if h_q <= 16 else (64 if h_q <= 64 else 128)
     n_hb = -(-h_q // RG)
     n_rg = s_q * n_hb
     Q = B * n_rg
     rng = np.random.default_rng(h_q + s_q)
-    n_splits = rng.integers(0, 5, Q)
+    n_splits = rng.integers(0, max_splits, Q)
     n_splits[0] = 3
     if Q > 2:
         n_splits[1] = 1
@@ -51,14 +54,20 @@ def test_combine_matches_oracle_merge(h_q, s_q, P):
     offs = np.zeros(Q + 1, dtype=np.int32)
     offs[1:] = np.cumsum(n_splits)
     S = Q + P
-    assert offs[-1] <= S
-    part_o = rng.standard_normal((S, RG, 512)).astype(np.float32)
+    assert offs[-1] <= S, (offs[-1], S)
+    # stored rows: fp16 values h with a power-of-two scale c per (slot, row), of
+    # magnitudes far apart; the partial the merge sees is c * h (exact in fp64)
+    part_h = rng.standard_normal((S, RG, 512)).astype(np.float16)
+    part_c = np.exp2(rng.integers(-30, 30, (S, RG))).astype(np.float32)
+    part_c[0, :3] = 1.0
+    part_o = part_h.astype(np.float64) * part_c[:, :, None].astype(np.float64)
     part_lse = (rng.standard_normal((S, RG)) * 3).astype(np.float32)
     part_lse[offs[0] + 1, :5] = -np.inf                     # an empty split
-    o_bytes = ((S * RG * 512 * 4 + 255) // 256) * 256
+    o_bytes = ((S * RG * 512 * 2 + 255) // 256) * 256
     ws = torch.zeros(mla.workspace_size(B, s_q, h_q, P), dtype=torch.uint8, device=dev)
-    ws[:S * RG * 512 * 4] = torch.from_numpy(_slot_layout(part_o).view(np.uint8).reshape(-1)).to(dev)
+    ws[:S * RG * 512 * 2] = torch.from_numpy(_slot_layout(part_h).view(np.uint8).reshape(-1)).to(dev)
     ws[o_bytes:o_bytes + S * RG * 4] = torch.from_numpy(part_lse.view(np.uint8).reshape(-1)).to(dev)
+    ws[o_bytes + S * RG * 4:o_bytes + 2 * S * RG * 4] = torch.from_numpy(part_c.view(np.uint8).reshape(-1)).to(dev)
     o = torch.full((B, s_q, h_q, 512), 7.0, dtype=torch.bfloat16, device=dev)   # sentinel
     lse = torch.full((B, s_q, h_q), 7.0, dtype=torch.float32, device=dev)
     q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=dev)
@@ -87,6 +96,7 @@ def test_combine_matches_oracle_merge(h_q, s_q, P):
                 assert np.all(og[b, i, h] == 0) and lg[b, i, h] == -np.inf
                 continue
             sl = slice(offs[qq], offs[qq + 1])
-            ro, rl = lse_merge(part_o[sl, r].astype(np.float64), part_lse[sl, r].astype(np.float64))
-            assert np.max(np.abs(og[b, i, h] - ro)) <= O_TOL
+            ro, rl = lse_merge(part_o[sl, r], part_lse[sl, r].astype(np.float64))
+            # relative to the row's magnitude (the scales span 2^-30 .. 2^29)
+            assert np.max(np.abs(og[b, i, h] - ro)) <= O_TOL * max(1.0, np.max(np.abs(ro)))
             assert abs(lg[b, i, h] - rl) <= LSE_RTOL * max(1.0, abs(rl))

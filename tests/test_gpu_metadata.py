@@ -13,13 +13,13 @@ pytestmark = pytest.mark.gpu
 
 # The documented policy (include/mla.h): row groups of 16 heads when h_q <= 16,
 # 64 when 16 < h_q <= 64, else 128; (fixed_cost, min_payload) = (0, 1) for 16,
-# (2, 2) for 64 and (2, 4) for 128.
+# (2, 2) for 64 and (2, 3) for 128.
 
 
 def _policy(h_q, s_q, batch, num_parts):
     if h_q <= 16:
         return (16, 0, 1)
-    return (64, 2, 2) if h_q <= 64 else (128, 2, 4)
+    return (64, 2, 2) if h_q <= 64 else (128, 2, 3)
 
 
 CASES = []
