@@ -113,14 +113,19 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
                 __builtin_amdgcn_make_buffer_rsrc((void*)(p.ws_scale + slot0 * RG), (short)0, nc * RG * 4, 0x00020000);
             float lv[kU], cv[kU];
             u32x2 v[kU][M::kVec];
+            // per-lane byte offsets in VGPRs, the split's offset in the
+            // (uniform) soffset field: no VGPR per load for addressing
             #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, (u * RG + row) * 4, 0, 0));
-                cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c_rs, (u * RG + row) * 4, 0, 0));
+                lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, row * 4, u * RG * 4, 0));
+                cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c_rs, row * 4, u * RG * 4, 0));
                 #pragma unroll
                 for (int j = 0; j < M::kVec; ++j)
-                    v[u][j] = __builtin_amdgcn_raw_buffer_load_b64(o_rs, u * kSlotBytes + f4[j] * 8, 0, AUX);
+                    v[u][j] = __builtin_amdgcn_raw_buffer_load_b64(o_rs, f4[j] * 8, u * kSlotBytes, AUX);
             }
+            // keep every load of the chunk ahead of the first use (left alone,
+            // the scheduler issues the data loads only after the lse maximum)
+            __builtin_amdgcn_sched_barrier(0);
             #pragma unroll
             for (int u = 0; u < kU; ++u)
                 if (u >= nc) lv[u] = -INFINITY;
