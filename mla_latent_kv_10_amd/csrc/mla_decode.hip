@@ -896,12 +896,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             // merge the four waves' states through LDS
             float l_w = l_run + wave_shfl_xor(l_run, 16);
             l_w += wave_shfl_xor(l_w, 32);
-            float LDS_AS* mo = (float LDS_AS*)smem;                  // [4][16][512]
-            float LDS_AS* mm = (float LDS_AS*)(smem + 4 * 16 * 512 * 4);  // [4][16] m, then [4][16] l
+            // [4][16][kMoStride]: rows padded by 4 floats, so the 16 rows a
+            // ds_write_b128 covers start 4 banks apart (at 512 floats every row
+            // began in the same bank: a 16-way conflict on every write)
+            constexpr int kMoStride = 516;
+            float LDS_AS* mo = (float LDS_AS*)smem;
+            float LDS_AS* mm = (float LDS_AS*)(smem + 4 * 16 * kMoStride * 4);  // [4][16] m, then [4][16] l
+            static_assert(4 * 16 * kMoStride * 4 + 2 * 64 * 4 <= S::kBytes, "merge buffers fit the tile area");
             const int row = lane & 15, g = lane >> 4;
             #pragma unroll
             for (int d = 0; d < 32; ++d)
-                *(f32x4 LDS_AS*)(mo + (wave * 16 + row) * 512 + 16 * d + 4 * g) = oacc[d];
+                *(f32x4 LDS_AS*)(mo + (wave * 16 + row) * kMoStride + 16 * d + 4 * g) = oacc[d];
             if (g == 0) { mm[wave * 16 + row] = m_run; mm[64 + wave * 16 + row] = l_w; }
             block_sync_lds();
             // thread -> row mr, dims 4c + 64j (j = 0..7): 16 threads cover 64 contiguous dims
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             for (int w = 0; w < 4; ++w) {
                 const float ew = e[w] * inv;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * 512 + c4 + 64 * j);
+                for (int j = 0; j < 8; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * kMoStride + c4 + 64 * j);
             }
             if (final_out) {
                 if (h < p.h_q) {
