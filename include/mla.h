@@ -64,7 +64,8 @@ extern "C" {
  *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
  *   MIN_PAYLOAD), the tile at position x goes to work part floor(x / W).
  *   FIXED_COST and MIN_PAYLOAD: RG 128 -> 2 and 3; RG 64 -> 2 and 2;
- *   RG 16 -> 0 and 1.
+ *   RG 16 -> 0 and 1; FIXED_COST is 0 for every RG when topk > 0 (all units
+ *   of a sparse call have the same tile count).
  *   Placement: when num_parts is a multiple of 8, with used = ceil(total / W)
  *   and k = ceil(used / 8), work part j is row (j / k) * (num_parts / 8) +
  *   j % k of tile_meta and every other row is empty (the decode grid runs

@@ -173,7 +173,10 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
     p.n_rg = l.n_rg;
     p.topk = topk;
     p.num_parts = num_parts;
-    p.fixed_cost = l.fixed_cost;
+    // A sparse call gives every row-group sequence the same tile count: a
+    // per-sequence fixed cost would only push part boundaries off sequence
+    // boundaries, so sparse calls use none.
+    p.fixed_cost = topk > 0 ? 0 : l.fixed_cost;
     p.min_payload = l.min_payload;
     hipError_t e = mla::launch_metadata(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "metadata launch: %s", hipGetErrorString(e));

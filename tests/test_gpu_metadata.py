@@ -13,13 +13,15 @@ pytestmark = pytest.mark.gpu
 
 # The documented policy (include/mla.h): row groups of 16 heads when h_q <= 16,
 # 64 when 16 < h_q <= 64, else 128; (fixed_cost, min_payload) = (0, 1) for 16,
-# (2, 2) for 64 and (2, 3) for 128.
+# (2, 2) for 64 and (2, 3) for 128, with fixed_cost 0 for sparse calls.
 
 
-def _policy(h_q, s_q, batch, num_parts):
+def _policy(h_q, s_q, batch, num_parts, topk):
     if h_q <= 16:
-        return (16, 0, 1)
-    return (64, 2, 2) if h_q <= 64 else (128, 2, 3)
+        rg, C, Wmin = 16, 0, 1
+    else:
+        rg, C, Wmin = (64, 2, 2) if h_q <= 64 else (128, 2, 3)
+    return rg, (0 if topk > 0 else C), Wmin
 
 
 CASES = []
@@ -46,7 +48,7 @@ def test_metadata_matches_reference(batch, s_q, h_q, num_parts, topk, seed):
     tm, so = mla.get_mla_metadata(seq if topk == 0 else None, s_q, h_q, topk=topk, num_parts=num_parts,
                                   batch=batch)
     torch.cuda.synchronize()
-    rg, C, Wmin = _policy(h_q, s_q, batch, num_parts)
+    rg, C, Wmin = _policy(h_q, s_q, batch, num_parts, topk)
     T = tile_counts(lens.tolist(), batch, s_q, h_q, topk, rg)
     ref_meta, ref_off = split_schedule(T, num_parts, C, Wmin)
     assert np.array_equal(so.cpu().numpy(), ref_off)
