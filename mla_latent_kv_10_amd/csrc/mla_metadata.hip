@@ -7,9 +7,9 @@
 // units laid end to end, fixed_cost positions then one per tile, work part
 // floor(position / W); then the work parts are placed on the grid so that the
 // ones holding work are spread evenly over the eight XCDs. One workgroup of
-// 256 threads computes it: block-wide exclusive scans built from wave
-// shuffles (positions with the last non-empty unit in one pass, then split
-// counts), then a binary search per part.
+// 256 threads computes it: block-wide exclusive scans built from DPP wave
+// scans with one barrier each (positions with the last non-empty unit in one
+// pass, then split counts), then a binary search per part.
 #include "mla_common.h"
 
 namespace mla {
@@ -24,66 +24,71 @@ enum ScanOp { kSum, kMax };
 template <ScanOp OP>
 __device__ __forceinline__ int combine(int a, int b) { return OP == kSum ? a + b : max(a, b); }
 
-// Exclusive scan of one value per thread across the workgroup (thread order);
-// `scratch` holds kWaves ints. *total receives the reduction over all threads.
+// One DPP move: lane i takes `v` from the lane the control names (row_shr:n
+// within rows of 16 lanes, row_bcast:15 / row_bcast:31 across rows). Lanes
+// whose source lies outside the pattern get an unspecified value; callers
+// use the result only in lanes where it is defined.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+
+// Inclusive scan of one value per lane across the wave64: doubling steps
+// inside each row of 16 lanes, then the last lane of rows 0 and 2 into rows 1
+// and 3, then lane 31 into rows 2 and 3. No LDS, no barrier.
+template <ScanOp OP>
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    const int lane = threadIdx.x & 63, rl = lane & 15;
+    int t;
+    t = dpp_mov<0x111>(x); if (rl >= 1) x = combine<OP>(t, x);   // row_shr:1
+    t = dpp_mov<0x112>(x); if (rl >= 2) x = combine<OP>(t, x);   // row_shr:2
+    t = dpp_mov<0x114>(x); if (rl >= 4) x = combine<OP>(t, x);   // row_shr:4
+    t = dpp_mov<0x118>(x); if (rl >= 8) x = combine<OP>(t, x);   // row_shr:8
+    t = dpp_mov<0x142>(x); if ((lane & 31) >= 16) x = combine<OP>(t, x);  // row_bcast:15
+    t = dpp_mov<0x143>(x); if (lane >= 32) x = combine<OP>(t, x);         // row_bcast:31
+    return x;
+}
+
+// Exclusive scan of one value per thread across the workgroup (thread order):
+// wave scans, then the wave totals through `scratch` (kWaves ints, used by
+// this scan only) behind one barrier. *total receives the reduction over all
+// threads.
 template <ScanOp OP>
 __device__ int block_exclusive_scan(int v, int identity, int* scratch, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int inc = v;
-    #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_up(inc, off, 64);
-        if (lane >= off) inc = combine<OP>(inc, u);
-    }
+    const int inc = wave_inclusive_scan<OP>(v);
     int exc = __shfl_up(inc, 1, 64);
     if (lane == 0) exc = identity;
     if (lane == 63) scratch[w] = inc;
     __syncthreads();
-    if (w == 0) {
-        int s = lane < kWaves ? scratch[lane] : identity;
-        #pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            const int u = __shfl_up(s, off, 64);
-            if (lane >= off) s = combine<OP>(s, u);
-        }
-        if (lane < kWaves) scratch[lane] = s;  // inclusive over waves
+    int before = identity, tot = identity;
+    #pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int s = scratch[i];
+        if (i < w) before = combine<OP>(before, s);
+        tot = combine<OP>(tot, s);
     }
-    __syncthreads();
-    const int before = w > 0 ? scratch[w - 1] : identity;
-    *total = scratch[kWaves - 1];
-    __syncthreads();
+    *total = tot;
     return combine<OP>(before, exc);
 }
 
-// Exclusive scans of two values per thread at once, a sum and a max, with one
-// set of barriers. Returns (sum before, max before); *sum_total receives the
-// sum over all threads.
+// Exclusive scans of two values per thread at once, a sum and a max, behind
+// one barrier (`scratch`: kWaves int2, used by this scan only). Returns (sum
+// before, max before); *sum_total receives the sum over all threads.
 __device__ int2 block_exclusive_scan_sum_max(int vs, int vm, int2* scratch, int* sum_total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int is = vs, im = vm;
-    #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int us = __shfl_up(is, off, 64), um = __shfl_up(im, off, 64);
-        if (lane >= off) { is += us; im = max(im, um); }
-    }
-    int es = __shfl_up(is, 1, 64), em = __shfl_up(im, 1, 64);
-    if (lane == 0) { es = 0; em = -1; }
+    const int is = wave_inclusive_scan<kSum>(vs), im = wave_inclusive_scan<kMax>(vm);
+    int es = is - vs, em = __shfl_up(im, 1, 64);
+    if (lane == 0) em = -1;
     if (lane == 63) scratch[w] = make_int2(is, im);
     __syncthreads();
-    if (w == 0) {
-        int2 v = lane < kWaves ? scratch[lane] : make_int2(0, -1);
-        #pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            const int us = __shfl_up(v.x, off, 64), um = __shfl_up(v.y, off, 64);
-            if (lane >= off) { v.x += us; v.y = max(v.y, um); }
-        }
-        if (lane < kWaves) scratch[lane] = v;  // inclusive over waves
+    int bs = 0, bm = -1, ts = 0;
+    #pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int2 s2 = scratch[i];
+        if (i < w) { bs += s2.x; bm = max(bm, s2.y); }
+        ts += s2.x;
     }
-    __syncthreads();
-    const int2 before = w > 0 ? scratch[w - 1] : make_int2(0, -1);
-    *sum_total = scratch[kWaves - 1].x;
-    __syncthreads();
-    return make_int2(before.x + es, max(before.y, em));
+    *sum_total = ts;
+    return make_int2(bs + es, max(bm, em));
 }
 
 // Smallest q in [0, n) with cum[q + 1] > v (cum has n + 1 entries, non-decreasing).
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
     __shared__ int s_cum[kMaxUnits + 1];    // exclusive scan of per-unit cost (positions)
     __shared__ int s_T[kMaxUnits];          // tiles per unit
     __shared__ int s_prev[kMaxUnits];       // last non-empty unit at or before q (-1 if none)
-    __shared__ int s_scan[kWaves];
-    __shared__ int2 s_scan2[kWaves];
+    __shared__ int s_scan[kWaves];    // wave totals of the split-count scan
+    __shared__ int2 s_scan2[kWaves];  // wave totals of the position scan
     const int Q = p.batch * p.n_rg;
     const int tid = threadIdx.x;
     const int C = p.fixed_cost;
