@@ -28,20 +28,25 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
-template <int RG>
+// VEC 4-value groups per thread per slot: 2, or 8 for the blocked layouts
+// when sequences have few splits (a quarter of the workgroups, each thread
+// doing four times the work).
+template <int RG, int VEC>
 struct CombineMap {
-    // blocks per row-group sequence, 4-value groups per thread per slot
-    static constexpr int kBlocksPerQ = RG == 16 ? 4 : RG / 4;  // 128 -> 32, 64 -> 16
-    static constexpr int kVec = 2;
+    static_assert(VEC == 2 || (VEC == 8 && RG != 16), "VEC 8 is for the blocked layouts");
+    static constexpr int kPerBlock = 16 / VEC;  // workgroups per 32-row block (blocked layouts)
+    // workgroups per row-group sequence: VEC 2 -> 32 (RG 128), 16 (RG 64), 4 (RG 16); VEC 8 -> 8, 4
+    static constexpr int kBlocksPerQ = RG == 16 ? 4 : (RG / 32) * kPerBlock;
+    static constexpr int kVec = VEC;
     // thread -> (row, group offsets within the slot, dims of each group)
     __device__ static void map(int blk, int t, int& row, int (&f4)[kVec], int (&dim)[kVec]) {
         if constexpr (RG != 16) {
-            const int w = blk >> 3, dq = blk & 7;
+            const int w = blk / kPerBlock, dq = blk % kPerBlock;
             const int lane = t & 63, g = (t >> 6) & 3;
             row = 32 * w + (lane & 31);
             #pragma unroll
             for (int j = 0; j < kVec; ++j) {
-                const int dd = 2 * dq + j;
+                const int dd = VEC * dq + j;
                 f4[j] = ((w * 16 + dd) * 4 + g) * 64 + lane;
                 dim[j] = 32 * dd + 8 * g + 4 * (lane >> 5);
             }
@@ -63,9 +68,9 @@ struct CombineMap {
 // the running reference m moves with a rescale of the sums, as in the online
 // softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} c_k h_k / s
 // with h_k the stored fp16 row, s = sum_k e^{lse_k - m}, lse = m + ln s.
-template <int RG>
+template <int RG, int VEC, int KU_MAX>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
-    using M = CombineMap<RG>;
+    using M = CombineMap<RG, VEC>;
     // XCD-aware numbering, as in the split kernel: the parts of one sequence
     // run on one XCD, so its partials are merged on the XCD that wrote them.
     int lb = blockIdx.x;
@@ -93,8 +98,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     // Each partial is read exactly once. With three or more splits the loads
     // are non-temporal (measured faster); with two (long sequences, many
     // workgroups) the default policy measured faster.
-    // kU splits in flight per chunk: the power of two in 2..16 nearest above n,
-    // so a sequence with few splits issues few loads.
+    // kU splits in flight per chunk: the power of two in 2..KU_MAX nearest
+    // above n, so a sequence with few splits issues few loads.
     auto merge = [&](auto nt_tag, auto ku_tag) {
         constexpr int AUX = decltype(nt_tag)::value ? 2 : 0;  // 2: nt
         constexpr int kU = decltype(ku_tag)::value;
@@ -156,9 +161,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     using I8 = std::integral_constant<int, 8>;
     using I16 = std::integral_constant<int, 16>;
     if (n <= 2) merge(std::false_type{}, I2{});
-    else if (n <= 4) merge(std::true_type{}, I4{});
-    else if (n <= 8) merge(std::true_type{}, I8{});
-    else merge(std::true_type{}, I16{});
+    else if (KU_MAX == 4 || n <= 4) merge(std::true_type{}, I4{});
+    else if constexpr (KU_MAX >= 16) {
+        if (n <= 8) merge(std::true_type{}, I8{});
+        else merge(std::true_type{}, I16{});
+    }
     // no split attended anything (or no split at all): o = 0, lse = -inf
     const bool empty = m == -INFINITY;
     const float inv = empty ? 0.f : 1.f / s;
@@ -174,14 +181,29 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 
 }  // namespace
 
+template <int RG, int VEC, int KU_MAX>
+void launch_map(const DecodeParams& p, int Q, hipStream_t s) {
+    hipLaunchKernelGGL((combine_kernel<RG, VEC, KU_MAX>), dim3((unsigned)Q * CombineMap<RG, VEC>::kBlocksPerQ), dim3(256),
+                       0, s, p);
+}
+
 hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
     const int Q = p.batch * p.n_rg;
+    // At most one split per sequence on average (num_parts <= Q): most rows
+    // were finished by the split kernel and the merge is mostly launch
+    // overhead, so the wide mapping (a quarter of the workgroups, chunks of up
+    // to 4 splits) is used. Any split count is merged correctly either way;
+    // this only picks the faster one (sparse prefill, one split per sequence:
+    // 21.4 -> 8.0 us; two splits per sequence: 11.6 -> 12.8 us, so not there).
+    const bool wide = p.num_parts <= Q;
     if (p.rg == 128) {
-        hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)Q * CombineMap<128>::kBlocksPerQ), dim3(256), 0, s, p);
+        if (wide) launch_map<128, 8, 4>(p, Q, s);
+        else launch_map<128, 2, 16>(p, Q, s);
     } else if (p.rg == 64) {
-        hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)Q * CombineMap<64>::kBlocksPerQ), dim3(256), 0, s, p);
+        if (wide) launch_map<64, 8, 4>(p, Q, s);
+        else launch_map<64, 2, 16>(p, Q, s);
     } else {
-        hipLaunchKernelGGL(combine_kernel<16>, dim3((unsigned)Q * CombineMap<16>::kBlocksPerQ), dim3(256), 0, s, p);
+        launch_map<16, 2, 16>(p, Q, s);
     }
     return hipGetLastError();
 }

@@ -35,10 +35,13 @@ def _slot_layout(part_o):
 
 @pytest.mark.parametrize("B,h_q,s_q,P,max_splits", [(3, 128, 1, 8, 5), (3, 64, 1, 64, 5), (3, 16, 2, 8, 5),
                                                    (3, 20, 1, 8, 5), (3, 100, 2, 8, 5), (10, 128, 1, 200, 40),
-                                                   (10, 16, 1, 200, 40), (6, 64, 2, 240, 40)])
+                                                   (10, 16, 1, 200, 40), (6, 64, 2, 240, 40), (8, 128, 1, 32, 9),
+                                                   (8, 64, 2, 48, 7), (48, 128, 1, 48, 3), (24, 64, 2, 48, 3)])
 def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     """Split counts 0..max_splits-1: every chunk size of the merge (2, 4, 8, 16
-    splits in flight) and sequences spanning several chunks."""
+    splits in flight), sequences spanning several chunks, and both thread
+    mappings of the blocked layouts (num_parts <= sequences selects the
+    wide one: 8 groups per thread, chunks of at most 4 splits)."""
     say(f"combine h_q={h_q} s_q={s_q} parts={P} splits<{max_splits}")
     dev = "cuda:0"
     RG = 16 if h_q <= 16 else (64 if h_q <= 64 else 128)
@@ -51,6 +54,8 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     if Q > 2:
         n_splits[1] = 1
         n_splits[2] = 0
+    if P <= Q and Q > 3:
+        n_splits[3] = 9   # the wide mapping: one sequence over three chunks
     offs = np.zeros(Q + 1, dtype=np.int32)
     offs[1:] = np.cumsum(n_splits)
     S = Q + P
