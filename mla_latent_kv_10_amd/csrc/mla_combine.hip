@@ -104,10 +104,11 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
         constexpr int AUX = decltype(nt_tag)::value ? 2 : 0;  // 2: nt
         constexpr int kU = decltype(ku_tag)::value;
         for (int k0 = 0; k0 < n; k0 += kU) {
-            // Buffer descriptors over this chunk's splits only: a load past the
-            // last split returns 0 without touching memory, so all kU loads
-            // issue unconditionally (a conditional load would become a branch
-            // closed by a wait, one round trip per split).
+            // All kU loads issue unconditionally (a conditional load would
+            // become a branch closed by a wait, one round trip per split).
+            // Slots past the chunk's last split re-read its first split and
+            // weigh zero: the split's offset travels in soffset, which the
+            // buffer range check does not cover, so it is chosen in range.
             const int nc = min(kU, n - k0);
             const int64_t slot0 = (int64_t)s0 + k0;
             const __amdgpu_buffer_rsrc_t o_rs =
@@ -122,11 +123,12 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
             // (uniform) soffset field: no VGPR per load for addressing
             #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, row * 4, u * RG * 4, 0));
-                cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c_rs, row * 4, u * RG * 4, 0));
+                const int su = u < nc ? u : 0;  // uniform
+                lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, row * 4, su * RG * 4, 0));
+                cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c_rs, row * 4, su * RG * 4, 0));
                 #pragma unroll
                 for (int j = 0; j < M::kVec; ++j)
-                    v[u][j] = __builtin_amdgcn_raw_buffer_load_b64(o_rs, f4[j] * 8, u * kSlotBytes, AUX);
+                    v[u][j] = __builtin_amdgcn_raw_buffer_load_b64(o_rs, f4[j] * 8, su * kSlotBytes, AUX);
             }
             // keep every load of the chunk ahead of the first use (left alone,
             // the scheduler issues the data loads only after the lse maximum)
