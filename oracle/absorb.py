@@ -14,7 +14,7 @@ What is computed (float64, from bf16 inputs):
     decode's query row (latent part first, RoPE part copied);
   * unabsorb_o: out[t, i] = W^UV_i o_lat[t, i], 128 values per head.
 
-Reading where the page is silent (also listed in the design doc): the RoPE part
+Reading where the page is silent: the RoPE part
 of the query is passed in already rotated; the absorbed query's first 512
 values are the latent dims and the last 64 the RoPE dims, the order of the
 cache row.

@@ -16,7 +16,7 @@ What is computed (for every batch b, query position i < s_q, head h):
     keeps S materialised).
   * lse is the natural log of the sum of exp(score) over attended tokens.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * causal alignment is bottom-right: query i sees cache positions
     t <= L - s_q + i;
   * an empty attended set gives o = 0 and lse = -inf;

@@ -18,7 +18,7 @@ What is computed, for one 576-value bf16 row [latent 512 ; rope 64]:
   * bytes [0, 512) codes, [512, 528) the four scales (little-endian fp32),
     [528, 656) the 64 rope values' bf16 bit patterns unchanged.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * the scale is amax / 448 in fp32, both divisions are IEEE fp32 divisions
     rounded to nearest even, and the quotient is clamped before it is rounded
     to e4m3 (the pages give the format and the 448 maximum, not the quantiser);
