@@ -41,7 +41,10 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     """Split counts 0..max_splits-1: every chunk size of the merge (2, 4, 8, 16
     splits in flight), sequences spanning several chunks, and both thread
     mappings of the blocked layouts (num_parts <= sequences selects the
-    wide one: 8 groups per thread, chunks of at most 4 splits)."""
+    wide one: 8 groups per thread, chunks of at most 4 splits). Workspace
+    bytes past the used slots hold NaN, and the last sequence's split count
+    is not a multiple of its chunk width, so a load slot past a chunk's last
+    split that read beyond the chunk would turn its zero weight into NaN."""
     say(f"combine h_q={h_q} s_q={s_q} parts={P} splits<{max_splits}")
     dev = "cuda:0"
     RG = 16 if h_q <= 16 else (64 if h_q <= 64 else 128)
@@ -56,6 +59,8 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
         n_splits[2] = 0
     if P <= Q and Q > 3:
         n_splits[3] = 9   # the wide mapping: one sequence over three chunks
+    if Q > 4:
+        n_splits[Q - 1] = 3   # chunk of 4 with one slot past the last split
     offs = np.zeros(Q + 1, dtype=np.int32)
     offs[1:] = np.cumsum(n_splits)
     S = Q + P
@@ -69,10 +74,16 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     part_lse = (rng.standard_normal((S, RG)) * 3).astype(np.float32)
     part_lse[offs[0] + 1, :5] = -np.inf                     # an empty split
     o_bytes = ((S * RG * 512 * 2 + 255) // 256) * 256
-    ws = torch.zeros(mla.workspace_size(B, s_q, h_q, P), dtype=torch.uint8, device=dev)
-    ws[:S * RG * 512 * 2] = torch.from_numpy(_slot_layout(part_h).view(np.uint8).reshape(-1)).to(dev)
-    ws[o_bytes:o_bytes + S * RG * 4] = torch.from_numpy(part_lse.view(np.uint8).reshape(-1)).to(dev)
-    ws[o_bytes + S * RG * 4:o_bytes + 2 * S * RG * 4] = torch.from_numpy(part_c.view(np.uint8).reshape(-1)).to(dev)
+    # only the slots the split offsets name are written; every other byte is
+    # 0xFF (NaN as fp16 and as fp32)
+    U = int(offs[-1])
+    ws_bytes = mla.workspace_size(B, s_q, h_q, P)
+    assert ws_bytes >= o_bytes + 2 * S * RG * 4
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device=dev)
+    ws[:U * RG * 512 * 2] = torch.from_numpy(_slot_layout(part_h)[:U].view(np.uint8).reshape(-1)).to(dev)
+    ws[o_bytes:o_bytes + U * RG * 4] = torch.from_numpy(part_lse[:U].view(np.uint8).reshape(-1)).to(dev)
+    ws[o_bytes + S * RG * 4:o_bytes + S * RG * 4 + U * RG * 4] = torch.from_numpy(
+        part_c[:U].view(np.uint8).reshape(-1)).to(dev)
     o = torch.full((B, s_q, h_q, 512), 7.0, dtype=torch.bfloat16, device=dev)   # sentinel
     lse = torch.full((B, s_q, h_q), 7.0, dtype=torch.float32, device=dev)
     q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=dev)
