@@ -1,0 +1,129 @@
+"""Graph replays of a decode step (metadata, split kernel, combine) reproduce the eager calls bit for bit.
+
+The benchmark times the path from captured graphs over rotating input sets.
+This test captures the same step for two input sets that differ in their
+queries and in their lengths or index sets (so the schedule differs too),
+then replays the graph several times with the outputs and workspaces
+poisoned, unrelated eager work and synchronisations between the replays.
+Every replay must give exactly the eager outputs: the kernels use no atomics
+and merge splits in a fixed order, so equal inputs give equal bits. The
+second set's eager result is also checked against the oracle on sampled rows.
+"""
+
+import ctypes
+import dataclasses
+
+import pytest
+import torch
+
+import mla_latent_kv_10_amd as mla
+from workload import config_workload, make_workload
+
+from tests.gpu_helpers import compare, oracle, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _second_set(w):
+    """Same cache; queries with heads rotated by one; dense: three quarters of
+    each length; sparse: every fifth index entry set to -1."""
+    q = w.q.roll(1, dims=2).contiguous()
+    seq, idx = w.cache_seqlens, w.indices
+    if idx is None:
+        seq = (seq * 3) // 4
+    else:
+        idx = idx.clone()
+        idx[..., ::5] = -1
+    return dataclasses.replace(w, q=q, cache_seqlens=seq, indices=idx, name=w.name + " (second set)")
+
+
+def _buffers(w, num_parts, dev, kv, bt):
+    n_meta, n_off = mla.metadata_size(w.batch, w.s_q, w.h_q, num_parts)
+    assert n_meta == num_parts * 8
+    d = {
+        "q": w.q.to(dev), "seq": w.cache_seqlens.to(dev),
+        "idx": None if w.indices is None else w.indices.to(dev),
+        "tm": torch.zeros((num_parts, 8), dtype=torch.int32, device=dev),
+        "so": torch.zeros((n_off,), dtype=torch.int32, device=dev),
+        "ws": torch.zeros((mla.workspace_size(w.batch, w.s_q, w.h_q, num_parts),), dtype=torch.uint8, device=dev),
+        "o": torch.zeros((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev),
+        "lse": torch.zeros((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev),
+    }
+    d["args"] = mla.make_args(d["q"], kv, bt, d["seq"], d["tm"], d["so"], w.softmax_scale, w.causal,
+                              w.kv_format == "fp8", d["idx"], d["ws"], d["o"], d["lse"])
+    return d
+
+
+def _step(L, w, d, num_parts, stream):
+    sp = 0 if d["idx"] is not None else d["seq"].data_ptr()
+    mla.check(L.mla_get_metadata(sp, w.batch, w.s_q, w.h_q, w.topk, num_parts, d["tm"].data_ptr(),
+                                 d["so"].data_ptr(), stream))
+    mla.check(L.mla_decode_with_kvcache(ctypes.byref(d["args"]), stream))
+
+
+def _poison(d):
+    d["o"].fill_(float("nan"))
+    d["lse"].fill_(float("nan"))
+    d["ws"].fill_(0xFF)
+
+
+def _same_bits(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+CASES = [(2, 8192, [(0, 0), (15, 0)]), (3, 16384, [(5, 0)]), (4, 8192, [(0, 1), (63, 0)]),
+         (5, 8192, [(0, 0), (31, 0)]), (6, 8192, [(0, 0), (0, 1023)])]
+
+
+@pytest.mark.parametrize("cfg,seqlen,rows", CASES, ids=[f"config{c[0]}" for c in CASES])
+def test_graph_replays_match_eager(cfg, seqlen, rows):
+    say(f"graph: config {cfg} (L={seqlen} where it applies), two input sets, {REPLAYS} replays")
+    dev = "cuda:0"
+    L = mla.lib()
+    w_a = config_workload(cfg, seqlen=seqlen)
+    w_b = _second_set(w_a)
+    num_parts = mla.default_num_parts(0)
+    kv = w_a.kv.to(dev)
+    bt = None if w_a.block_table is None else w_a.block_table.to(dev)
+    sets = [(w_a, _buffers(w_a, num_parts, dev, kv, bt)), (w_b, _buffers(w_b, num_parts, dev, kv, bt))]
+    stream = torch.cuda.Stream(device=dev)
+
+    # eager results, twice: the path itself must be deterministic
+    refs = []
+    for w, d in sets:
+        outs = []
+        for _ in range(2):
+            _poison(d)
+            torch.cuda.synchronize()   # the fills run on another stream than the step
+            with torch.cuda.stream(stream):
+                _step(L, w, d, num_parts, stream.cuda_stream)
+            torch.cuda.synchronize()
+            outs.append((d["o"].clone(), d["lse"].clone()))
+        assert _same_bits(outs[0][0], outs[1][0]) and _same_bits(outs[0][1], outs[1][1]), w.name
+        refs.append(outs[0])
+
+    o_ref, lse_ref = oracle(w_b, rows)
+    compare(refs[1][0], refs[1][1], o_ref, lse_ref, rows, label=w_b.name)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for w, d in sets:
+            _step(L, w, d, num_parts, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+    other = make_workload(batch=2, s_q=1, h_q=64, seqlens=[300, 77], kv_format="bf16", seed=5)
+    for r in range(REPLAYS):
+        for _, d in sets:
+            _poison(d)
+        run_gpu(other)                 # unrelated eager work between replays
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        for (w, d), (o0, l0) in zip(sets, refs):
+            assert _same_bits(d["o"], o0), f"replay {r}: o differs from eager for {w.name}"
+            assert _same_bits(d["lse"], l0), f"replay {r}: lse differs from eager for {w.name}"
+        say(f"  replay {r}: both sets equal to eager")
