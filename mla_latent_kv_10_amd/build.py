@@ -33,7 +33,15 @@ COMMON_FLAGS = [
 
 # The decode kernel keeps MFMA accumulators of the score tile in VGPRs
 # (VGPR form) and pins the output accumulator to AGPRs with inline asm.
-EXTRA_FLAGS = {"mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Kernel-argument preload (SGPRs filled at dispatch; the count is in arguments)
+# for the combine (one leading pointer) and the schedule kernel (nine
+# scalars). The split kernel does not use it: preloading its schedule pointer
+# measured slower.
+EXTRA_FLAGS = {
+    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "mla_combine.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=1"],
+    "mla_metadata.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
+}
 
 
 def _hipcc() -> str:

@@ -69,7 +69,10 @@ struct CombineMap {
 // softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} c_k h_k / s
 // with h_k the stored fp16 row, s = sum_k e^{lse_k - m}, lse = m + ln s.
 template <int RG, int VEC, int KU_MAX>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+// split_offsets travels as a separate leading argument (the same pointer as
+// p.split_offsets), preloaded into SGPRs at dispatch, so the split-count
+// loads issue without waiting for the argument block.
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ split_offsets, DecodeParams p) {
     using M = CombineMap<RG, VEC>;
     // XCD-aware numbering, as in the split kernel: the parts of one sequence
     // run on one XCD, so its partials are merged on the XCD that wrote them.
@@ -84,8 +87,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     M::map(blk, threadIdx.x, row, f4, dim);
     const int h = (rgi - i * p.n_hb) * RG + row;
     if (h >= p.h_q) return;
-    const int s0 = p.split_offsets[q];
-    const int n = p.split_offsets[q + 1] - s0;
+    const int s0 = split_offsets[q];
+    const int n = split_offsets[q + 1] - s0;
     if (n == 1) return;  // the split kernel wrote the final row
     const int64_t orow = ((int64_t)b * p.s_q + i) * p.h_q + h;
     uint16_t* op = p.o + orow * kDv;
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 template <int RG, int VEC, int KU_MAX>
 void launch_map(const DecodeParams& p, int Q, hipStream_t s) {
     hipLaunchKernelGGL((combine_kernel<RG, VEC, KU_MAX>), dim3((unsigned)Q * CombineMap<RG, VEC>::kBlocksPerQ), dim3(256),
-                       0, s, p);
+                       0, s, p.split_offsets, p);
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {

@@ -101,7 +101,12 @@ __device__ int first_unit_past(const int* cum, int n, int v) {
     return lo;
 }
 
-__global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
+// Scalar arguments rather than one struct: they are preloaded into SGPRs at
+// dispatch, so the length loads issue without waiting for the argument block.
+__global__ __launch_bounds__(kMT) void metadata_kernel(const int32_t* seqlens, int32_t* tile_meta, int32_t* split_offsets,
+                                                       int batch, int n_rg, int topk, int num_parts, int fixed_cost,
+                                                       int min_payload) {
+    const MetaParams p{seqlens, tile_meta, split_offsets, batch, n_rg, topk, num_parts, fixed_cost, min_payload};
     __shared__ int s_cum[kMaxUnits + 1];    // exclusive scan of per-unit cost (positions)
     __shared__ int s_T[kMaxUnits];          // tiles per unit
     __shared__ int s_prev[kMaxUnits];       // last non-empty unit at or before q (-1 if none)
@@ -216,7 +221,8 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(MetaParams p) {
 }  // namespace
 
 hipError_t launch_metadata(const MetaParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMT), 0, s, p);
+    hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMT), 0, s, p.seqlens, p.tile_meta, p.split_offsets, p.batch,
+                       p.n_rg, p.topk, p.num_parts, p.fixed_cost, p.min_payload);
     return hipGetLastError();
 }
 
