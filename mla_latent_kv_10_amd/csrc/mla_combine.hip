@@ -68,10 +68,10 @@ struct CombineMap {
 // the running reference m moves with a rescale of the sums, as in the online
 // softmax ([Walkthrough] §五). Result: o = sum_k e^{lse_k - m} c_k h_k / s
 // with h_k the stored fp16 row, s = sum_k e^{lse_k - m}, lse = m + ln s.
-template <int RG, int VEC, int KU_MAX>
 // split_offsets travels as a separate leading argument (the same pointer as
 // p.split_offsets), preloaded into SGPRs at dispatch, so the split-count
 // loads issue without waiting for the argument block.
+template <int RG, int VEC, int KU_MAX>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ split_offsets, DecodeParams p) {
     using M = CombineMap<RG, VEC>;
     // XCD-aware numbering, as in the split kernel: the parts of one sequence
