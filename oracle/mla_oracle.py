@@ -22,6 +22,8 @@ Readings where the pages are silent:
   * an empty attended set gives o = 0 and lse = -inf;
   * a sparse index outside [0, num_rows) is treated like -1 (skipped);
     duplicate indices each count;
+  * a dense position whose page id is not a cache page (e.g. -1), or past
+    the block table's row, is skipped in the same way;
   * FP8 rows dequantise as bf16_rne(fp32(code) * fp32(scale)), the product
     rounded once to fp32, then once to bf16.
 """
@@ -126,6 +128,10 @@ def attended_rows(
 
     Dense: positions t < L_b (causal: t <= L_b - s_q + i); position t lives in
     page block_table[b, t // 64] at offset t % 64, i.e. row page*64 + t%64.
+    A position whose page id is not a page of the cache (outside
+    [0, num_rows / 64), e.g. -1) or that lies past the block table's row
+    (t >= 64 * max_blocks_per_seq) has no cache row and is skipped: the pages
+    never say what such a slot holds, so it is read as absent.
     Sparse ([Walkthrough] §八 "当前 master 已经是稀疏注意力"; [Guide]
     §"怎么用起来"): the listed absolute rows page*block_size + offset; -1
     entries are skipped, and so is anything outside [0, num_rows).
@@ -136,9 +142,12 @@ def attended_rows(
     L = int(cache_seqlens[b])
     limit = L - s_q + 1 + i if causal else L
     limit = max(0, min(limit, L))
+    table = np.asarray(block_table[b], dtype=np.int64)
+    limit = min(limit, table.shape[0] * BLOCK_SIZE)
     t = np.arange(limit, dtype=np.int64)
-    pages = np.asarray(block_table[b], dtype=np.int64)[t // BLOCK_SIZE]
-    return pages * BLOCK_SIZE + t % BLOCK_SIZE
+    pages = table[t // BLOCK_SIZE]
+    keep = (pages >= 0) & (pages < num_rows // BLOCK_SIZE)
+    return pages[keep] * BLOCK_SIZE + t[keep] % BLOCK_SIZE
 
 
 # --------------------------------------------------------------------------

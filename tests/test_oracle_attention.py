@@ -198,6 +198,32 @@ def test_empty_sets():
     assert np.all(o == 0) and np.all(l == -np.inf)
 
 
+def test_invalid_pages_and_positions_past_the_table_are_skipped():
+    """Dense positions whose page id names no cache page (-1, or a page past
+    the pool) and positions past the block table's row contribute nothing:
+    o and lse equal library softmax / logsumexp over the scores of the
+    remaining tokens, gathered by hand."""
+    rng = np.random.default_rng(12)
+    rows, bt = _paged(rng, [300], num_extra=2)   # 5 pages of 64 in a pool of 7
+    pool = rows.shape[0] // 64
+    q = rng.standard_normal((1, 1, 3, 576))
+
+    def check(table, L, kept_positions):
+        o, lse = _run(q, rows, table, [L])
+        K = rows[[int(bt[0, t // 64]) * 64 + t % 64 for t in kept_positions]]
+        for h in range(3):
+            s = SCALE * (K @ q[0, 0, h])
+            assert np.max(np.abs(o[0, 0, h] - scipy.special.softmax(s) @ K[:, :512])) < 1e-12
+            assert abs(lse[0, 0, h] - scipy.special.logsumexp(s)) < 1e-12
+
+    bad = bt.copy()
+    bad[0, 1] = -1          # positions 64..127
+    bad[0, 3] = pool + 2    # positions 192..255: a page id past the cache
+    check(bad, 300, [t for t in range(300) if t // 64 in (0, 2, 4)])
+    # a block table of two pages holds positions 0..127 only, whatever L says
+    check(np.ascontiguousarray(bt[:, :2]), 200, list(range(128)))
+
+
 def test_attended_rows_dense_mapping():
     bt = np.array([[3, 0, 7]])
     r = attended_rows(0, 0, s_q=1, num_rows=8 * 64, block_table=bt, cache_seqlens=np.array([130]),

@@ -67,6 +67,28 @@ def _rows_keep_minus_one(b, i, *, s_q, num_rows, block_table, cache_seqlens, cau
                                cache_seqlens=cache_seqlens, causal=causal, indices=indices)
 
 
+def _rows_wrap_invalid_pages(b, i, *, s_q, num_rows, block_table, cache_seqlens, causal, indices):
+    if indices is None:
+        L = int(cache_seqlens[b])
+        t = np.arange(L)
+        pages = np.asarray(block_table[b])[np.minimum(t // 64, len(block_table[b]) - 1)]
+        return (pages % (num_rows // 64)) * 64 + t % 64  # reads some page for -1 / out-of-pool ids
+    return _real_attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
+                               cache_seqlens=cache_seqlens, causal=causal, indices=indices)
+
+
+def _rows_past_table_reuse_last_page(b, i, *, s_q, num_rows, block_table, cache_seqlens, causal, indices):
+    if indices is None and not causal:
+        L = int(cache_seqlens[b])
+        t = np.arange(L)
+        table = np.asarray(block_table[b])
+        pages = table[np.minimum(t // 64, len(table) - 1)]
+        keep = (pages >= 0) & (pages < num_rows // 64)
+        return pages[keep] * 64 + t[keep] % 64
+    return _real_attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
+                               cache_seqlens=cache_seqlens, causal=causal, indices=indices)
+
+
 _real_decode = om.decode_rows
 
 
@@ -102,6 +124,7 @@ ATTENTION_PINS = [
     ta.test_causal_alignment,
     ta.test_page_permutation_invariance,
     ta.test_sparse_all_rows_equals_dense_and_ignores_invalid,
+    ta.test_invalid_pages_and_positions_past_the_table_are_skipped,
 ]
 
 
@@ -112,7 +135,8 @@ def test_attend_mutants_are_caught(monkeypatch, mutant):
     assert any(_fails(p) for p in ATTENTION_PINS)
 
 
-@pytest.mark.parametrize("mutant", [_rows_causal_off_by_one, _rows_ignore_block_table, _rows_keep_minus_one])
+@pytest.mark.parametrize("mutant", [_rows_causal_off_by_one, _rows_ignore_block_table, _rows_keep_minus_one,
+                                    _rows_wrap_invalid_pages, _rows_past_table_reuse_last_page])
 def test_masking_mutants_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(om, "attended_rows", mutant)
     assert any(_fails(p) for p in ATTENTION_PINS)
