@@ -50,6 +50,9 @@ extern "C" {
 #define MLA_D_QK 576
 #define MLA_D_V 512
 #define MLA_MAX_UNITS 8192 /* max row-group sequences (see below) per call */
+#define MLA_MAX_SEQ_TOKENS (1 << 23) /* tokens one sequence may attend: cache_seqlens
+                                        entries above it read as this value; bounds
+                                        max_blocks_per_seq (2^17 pages) and topk */
 
 /*
  * Split policy (the library's own rule; the pages give the metadata's role,
@@ -119,7 +122,8 @@ int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes
  * num_parts). Reusing it after any of these change gives wrong splits
  * silently; the caller must recompute it ([Walkthrough] §七 warns the same).
  * Errors: MLA_ERR_INVALID for null buffers, batch/s_q/h_q < 1, topk < 0,
- * num_parts out of range; MLA_ERR_UNSUPPORTED if Q > MLA_MAX_UNITS.
+ * num_parts out of range; MLA_ERR_UNSUPPORTED if Q > MLA_MAX_UNITS or
+ * topk > MLA_MAX_SEQ_TOKENS.
  */
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int topk,
                      int num_parts, int32_t* tile_meta, int32_t* split_offsets, void* stream);
@@ -130,7 +134,9 @@ typedef struct mla_decode_args {
     const void* q;             /* device bf16 [batch, s_q, h_q, 576]: absorbed latent
                                   query (512) then rope query (64) */
     const void* kv;            /* device uint8 [num_blocks, 64, row_bytes] */
-    int64_t num_blocks;        /* pages in the cache; num_blocks*64 < 2^31 */
+    int64_t num_blocks;        /* pages in the cache; num_blocks * 64 * row_bytes
+                                  <= 2^32 (4 GiB: rows are addressed with 32-bit
+                                  byte offsets from kv) */
     int32_t block_size;        /* must be 64 */
     int32_t row_bytes;         /* 1152 for MLA_KV_BF16, 656 for MLA_KV_FP8_656; a
                                   mismatch is rejected ([Guide] §"容易踩的坑") */
@@ -138,13 +144,14 @@ typedef struct mla_decode_args {
     const int32_t* block_table;   /* dense: device int32 [batch, max_blocks_per_seq];
                                      token t of sequence b is row
                                      block_table[b, t/64]*64 + t%64 */
-    int32_t max_blocks_per_seq;
+    int32_t max_blocks_per_seq;   /* 1 .. MLA_MAX_SEQ_TOKENS / 64 */
     const int32_t* cache_seqlens; /* dense: device int32 [batch], tokens per sequence */
     const int32_t* indices;       /* sparse: device int32 [batch, s_q, topk] absolute
                                      cache rows (page*64 + offset), -1 = unused
                                      ([Walkthrough] §八 "当前 master 已经是稀疏注意力");
                                      NULL selects dense attention */
-    int32_t topk;
+    int32_t topk;              /* sparse: 1 .. MLA_MAX_SEQ_TOKENS, with
+                                  batch * s_q * topk < 2^29 */
     float softmax_scale;
     int32_t causal;            /* dense only: query i sees t <= L - s_q + i.
                                   causal with indices -> MLA_ERR_INVALID
@@ -165,7 +172,9 @@ typedef struct mla_decode_args {
  * is outside [0, num_blocks) or past max_blocks_per_seq) are never read and
  * never contribute. A query row with no attended token gets o = 0 and
  * lse = -inf. Errors: MLA_ERR_INVALID (see field notes), MLA_ERR_WORKSPACE,
- * MLA_ERR_UNSUPPORTED, MLA_ERR_HIP.
+ * MLA_ERR_UNSUPPORTED (block_size other than 64, a cache above 4 GiB,
+ * max_blocks_per_seq or topk above their bounds, Q > MLA_MAX_UNITS),
+ * MLA_ERR_HIP.
  */
 int mla_decode_with_kvcache(const mla_decode_args* args, void* stream);
 

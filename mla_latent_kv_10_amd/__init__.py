@@ -167,6 +167,17 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be contiguous")
 
 
+def _expect(t, label: str, dtype, shape) -> None:
+    """t must have this dtype and shape (None in shape: any size there)."""
+    if t is None:
+        raise ValueError(f"{label} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{label} must be {dtype} (got {t.dtype})")
+    if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+        want = ", ".join("*" if w is None else str(w) for w in shape)
+        raise ValueError(f"{label} must have shape [{want}] (got {list(t.shape)})")
+
+
 def get_mla_metadata(cache_seqlens, s_q: int, h_q: int, topk: int = 0, num_parts: Optional[int] = None,
                      batch: Optional[int] = None):
     """Split schedule for one decode step; returns (tile_meta, split_offsets) int32 GPU tensors."""
@@ -186,32 +197,73 @@ def get_mla_metadata(cache_seqlens, s_q: int, h_q: int, topk: int = 0, num_parts
     split_offsets = torch.empty((n_off,), dtype=torch.int32, device=device)
     check(lib().mla_get_metadata(_ptr(cache_seqlens), batch, s_q, h_q, topk, num_parts, tile_meta.data_ptr(),
                                  split_offsets.data_ptr(), _stream_handle(device)))
+    # the call shape the schedule was built for; the decode compares it
+    tile_meta.mla_call_shape = (batch, s_q, h_q, topk)
     return tile_meta, split_offsets
 
 
 def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softmax_scale, causal, is_fp8_kvcache,
               indices, workspace, o, lse) -> MlaDecodeArgs:
-    batch, s_q, h_q, d = q.shape
-    if d != 576:
-        raise ValueError("q must be [batch, s_q, h_q, 576]")
-    row_bytes = kv[0, 0].numel() * kv.element_size()
+    """Argument block for the decode entry points, after checking every tensor.
+
+    q bf16 [B, s_q, h_q, 576]; kv [num_blocks, 64, 576] bf16 or [num_blocks,
+    64, 1152] uint8 (bf16 cache), [num_blocks, 64, 656] uint8 (FP8 cache);
+    dense: block_table int32 [B, max_blocks_per_seq] and cache_seqlens int32
+    [B]; sparse: indices int32 [B, s_q, topk]; tile_meta int32 [num_parts, 8]
+    and split_offsets int32 [Q + 1] from get_mla_metadata for this (B, s_q,
+    h_q, topk); workspace uint8 with at least workspace_size(...) bytes; o bf16
+    [B, s_q, h_q, 512]; lse fp32 [B, s_q, h_q]. All contiguous, on q's device.
+    Raises ValueError naming the first tensor that does not fit.
+    """
+    torch = _torch()
+    _expect(q, "q", torch.bfloat16, (None, None, None, 576))
+    batch, s_q, h_q, _ = q.shape
+    if is_fp8_kvcache:
+        _expect(kv, "kv (FP8 cache)", torch.uint8, (None, 64, 656))
+    elif kv is not None and kv.dtype == torch.bfloat16:
+        _expect(kv, "kv (bf16 cache)", torch.bfloat16, (None, 64, 576))
+    else:
+        _expect(kv, "kv (bf16 cache as bytes)", torch.uint8, (None, 64, 1152))
+    if indices is None:
+        _expect(block_table, "block_table", torch.int32, (batch, None))
+        _expect(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
+        topk = 0
+    else:
+        _expect(indices, "indices", torch.int32, (batch, s_q, None))
+        topk = indices.shape[2]
+    _expect(tile_meta, "tile_meta", torch.int32, (None, 8))
+    num_parts = tile_meta.shape[0]
+    _, n_off = metadata_size(batch, s_q, h_q, num_parts)
+    _expect(split_offsets, "split_offsets", torch.int32, (n_off,))
+    built = getattr(tile_meta, "mla_call_shape", None)
+    if built is not None and tuple(built) != (batch, s_q, h_q, topk):
+        raise ValueError(f"metadata was built for (batch, s_q, h_q, topk) = {tuple(built)}, "
+                         f"this call is {(batch, s_q, h_q, topk)}: call get_mla_metadata again")
+    _expect(workspace, "workspace", torch.uint8, (None,))
+    _expect(o, "o", torch.bfloat16, (batch, s_q, h_q, 512))
+    _expect(lse, "lse", torch.float32, (batch, s_q, h_q))
+    tensors = [q, kv, tile_meta, split_offsets, workspace, o, lse]
+    tensors += [block_table, cache_seqlens] if indices is None else [indices]
+    _require_gpu(*tensors)
+    if any(t.device != q.device for t in tensors):
+        raise ValueError("all tensors must be on q's device")
     a = MlaDecodeArgs()
     a.struct_size = ctypes.sizeof(MlaDecodeArgs)
     a.batch, a.s_q, a.h_q = batch, s_q, h_q
     a.q, a.kv = q.data_ptr(), kv.data_ptr()
     a.num_blocks = kv.shape[0]
     a.block_size = kv.shape[1]
-    a.row_bytes = row_bytes
+    a.row_bytes = kv[0, 0].numel() * kv.element_size()
     a.kv_format = MLA_KV_FP8_656 if is_fp8_kvcache else MLA_KV_BF16
     a.block_table = _ptr(block_table) if indices is None else 0
-    a.max_blocks_per_seq = block_table.shape[1] if (block_table is not None and indices is None) else 0
+    a.max_blocks_per_seq = block_table.shape[1] if indices is None else 0
     a.cache_seqlens = _ptr(cache_seqlens) if indices is None else 0
     a.indices = _ptr(indices)
-    a.topk = indices.shape[2] if indices is not None else 0
+    a.topk = topk
     a.softmax_scale = float(softmax_scale)
     a.causal = 1 if causal else 0
     a.tile_meta, a.split_offsets = tile_meta.data_ptr(), split_offsets.data_ptr()
-    a.num_parts = tile_meta.shape[0]
+    a.num_parts = num_parts
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.o, a.lse = o.data_ptr(), lse.data_ptr()
@@ -225,10 +277,8 @@ def mla_decode_with_kvcache(q, kv, block_table, cache_seqlens, head_dim_v: int, 
     torch = _torch()
     if head_dim_v != 512:
         raise ValueError("head_dim_v must be 512")
-    if q.dtype != torch.bfloat16:
-        raise ValueError("q must be bfloat16")
-    _require_gpu(q, kv, block_table if indices is None else None, cache_seqlens if indices is None else None,
-                 indices, tile_meta, split_offsets)
+    _expect(q, "q", torch.bfloat16, (None, None, None, 576))
+    _expect(tile_meta, "tile_meta", torch.int32, (None, 8))
     batch, s_q, h_q, _ = q.shape
     if softmax_scale is None:
         softmax_scale = 576 ** -0.5

@@ -73,14 +73,25 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (a->num_blocks < 1) return fail(MLA_ERR_INVALID, "num_blocks must be >= 1");
     if (a->num_blocks * (int64_t)mla::kBlock >= ((int64_t)1 << 31))
         return fail(MLA_ERR_UNSUPPORTED, "num_blocks * 64 must be < 2^31");
+    // the split kernel addresses rows through buffer descriptors, whose byte
+    // offsets are 32-bit: the whole cache must lie within 4 GiB of its start
+    if (a->num_blocks * (int64_t)mla::kBlock * a->row_bytes > ((int64_t)1 << 32))
+        return fail(MLA_ERR_UNSUPPORTED, "the cache (num_blocks * 64 * row_bytes = %lld bytes) must be at most 4 GiB",
+                    (long long)(a->num_blocks * (int64_t)mla::kBlock * a->row_bytes));
     const bool sparse = a->indices != nullptr;
     if (sparse) {
         if (a->topk < 1) return fail(MLA_ERR_INVALID, "topk must be >= 1 with indices");
         if (a->causal) return fail(MLA_ERR_INVALID, "causal masking is not defined with sparse indices");
+        if (a->topk > mla::kMaxSeqTokens)
+            return fail(MLA_ERR_UNSUPPORTED, "topk must be <= 2^23 (got %d)", a->topk);
+        if ((int64_t)a->batch * a->s_q * a->topk >= ((int64_t)1 << 29))
+            return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * topk must be < 2^29 index entries");
     } else {
         if (!a->block_table || !a->cache_seqlens)
             return fail(MLA_ERR_INVALID, "dense attention needs block_table and cache_seqlens");
         if (a->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+        if (a->max_blocks_per_seq > mla::kMaxSeqTokens / mla::kBlock)
+            return fail(MLA_ERR_UNSUPPORTED, "max_blocks_per_seq must be <= 2^17 (got %d)", a->max_blocks_per_seq);
         if (a->topk != 0) return fail(MLA_ERR_INVALID, "topk must be 0 without indices");
     }
     if (!std::isfinite(a->softmax_scale)) return fail(MLA_ERR_INVALID, "softmax_scale must be finite");
@@ -161,6 +172,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
     int st = check_shape(batch, s_q, h_q, num_parts);
     if (st) return st;
     if (topk < 0) return fail(MLA_ERR_INVALID, "topk must be >= 0 (got %d)", topk);
+    if (topk > mla::kMaxSeqTokens) return fail(MLA_ERR_UNSUPPORTED, "topk must be <= 2^23 (got %d)", topk);
     if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
     if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
     if (!aligned(tile_meta, 16)) return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned");

@@ -20,6 +20,11 @@ constexpr int kRawRow = 656;        // FP8 row ([Guide] §"FP8 缓存怎么把 K
 constexpr int kRawUnits = 41;       // 656 / 16
 constexpr int kRawTileBytes = kBlock * kRawRow; // one FP8 tile as stored, 41 x 1 KB
 constexpr int kMaxUnits = 8192;     // row-group sequences per call (metadata LDS)
+// Longest sequence a call attends (tokens): cache_seqlens entries above it are
+// read as this value, max_blocks_per_seq and topk are bounded by it. With at
+// most kMaxUnits sequences of at most 2^17 tiles, every schedule position
+// and tile index stays below 2^31.
+constexpr int kMaxSeqTokens = 1 << 23;
 constexpr int kThreads = 256;       // four wave64s per workgroup
 
 enum Variant { kV128 = 0, kV16 = 1, kV64 = 2 };

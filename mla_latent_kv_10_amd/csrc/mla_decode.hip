@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // Sparse, FP8, 128-head groups: the index words travel to the LDS ring
         // (every wave loads the whole slot and reads only what it loaded), so
         // no register carries a pending load across tile-loop iterations.
+        // batch * s_q * topk < 2^29 (checked on the host): byte offsets fit 32 bits
         const u32x4 ix_words = make_rsrc_words(p.indices, 0, (unsigned)(p.batch * p.s_q * p.topk) * 4u);
         const int ix_row0 = ((sg.b * p.s_q + sg.i) * p.topk);
         auto ring_load = [&](int k) {
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             T_q = (p.topk + kBlock - 1) / kBlock;
             sg.limit = p.topk;
         } else {
-            const int L = uniform(len_raw);
+            const int L = min(uniform(len_raw), kMaxSeqTokens);  // as the schedule reads it
             T_q = L > 0 ? (L + kBlock - 1) / kBlock : 0;
             int lim = p.causal ? L - p.s_q + 1 + sg.i : L;
             lim = min(lim, min(L, p.mbps * kBlock));

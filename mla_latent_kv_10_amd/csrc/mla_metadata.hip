@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kMT) void metadata_kernel(const int32_t* seqlens, i
         if (p.topk > 0) {
             T = (p.topk + kBlock - 1) / kBlock;
         } else {
-            const int L = p.seqlens[q / p.n_rg];
+            const int L = min(p.seqlens[q / p.n_rg], kMaxSeqTokens);
             T = L > 0 ? (L + kBlock - 1) / kBlock : 0;
         }
         s_T[q] = T;

@@ -11,7 +11,8 @@ assignment (the GPU computes the same result per part, in parallel):
 
   * Work units are "row-group sequences" q = b * n_rg + rg, rg = i * n_hb + hb
     (query position i, head block hb of rg_rows heads). Unit q has T_q tiles
-    of 64 tokens: ceil(L_b / 64) dense, ceil(topk / 64) sparse.
+    of 64 tokens: ceil(L_b / 64) dense, ceil(topk / 64) sparse, with L_b read
+    as at most 2^23 (the longest sequence a call attends).
   * Units are laid end to end on a line; a non-empty unit first takes
     fixed_cost positions (its per-split overhead), then one position per tile.
   * With total = sum over non-empty units of (fixed_cost + T_q) and
@@ -34,6 +35,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 BLOCK_SIZE = 64
+MAX_SEQ_TOKENS = 1 << 23
 
 
 def tile_counts(cache_seqlens: Optional[Sequence[int]], batch: int, s_q: int, h_q: int,
@@ -43,7 +45,8 @@ def tile_counts(cache_seqlens: Optional[Sequence[int]], batch: int, s_q: int, h_
     n_rg = s_q * n_hb
     out = []
     for b in range(batch):
-        T = -(-topk // BLOCK_SIZE) if topk > 0 else -(-max(int(cache_seqlens[b]), 0) // BLOCK_SIZE)
+        L = min(max(int(cache_seqlens[b]), 0), MAX_SEQ_TOKENS)
+        T = -(-topk // BLOCK_SIZE) if topk > 0 else -(-L // BLOCK_SIZE)
         out.extend([T] * n_rg)
     return out
 

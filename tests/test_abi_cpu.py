@@ -124,6 +124,9 @@ CASES = [
     (dict(row_bytes=656), m.MLA_ERR_INVALID, "row_bytes"),                    # fp8 rows flagged bf16
     (dict(num_blocks=0), m.MLA_ERR_INVALID, "num_blocks"),
     (dict(num_blocks=1 << 26), m.MLA_ERR_UNSUPPORTED, "2^31"),
+    (dict(num_blocks=(1 << 32) // (64 * 1152) + 1), m.MLA_ERR_UNSUPPORTED, "4 GiB"),
+    (dict(num_blocks=(1 << 32) // (64 * 656) + 1, kv_format=m.MLA_KV_FP8_656, row_bytes=656),
+     m.MLA_ERR_UNSUPPORTED, "4 GiB"),
     (dict(indices=FAKE, topk=0, block_table=0, cache_seqlens=0), m.MLA_ERR_INVALID, "topk"),
     (dict(indices=FAKE, topk=64, causal=1), m.MLA_ERR_INVALID, "causal"),
     (dict(block_table=0), m.MLA_ERR_INVALID, "block_table"),
@@ -136,6 +139,9 @@ CASES = [
     (dict(workspace_bytes=16), m.MLA_ERR_WORKSPACE, "workspace_bytes"),
     (dict(batch=0), m.MLA_ERR_INVALID, "batch"),
     (dict(h_q=0), m.MLA_ERR_INVALID, "h_q"),
+    (dict(indices=FAKE, topk=(1 << 23) + 1, block_table=0, cache_seqlens=0), m.MLA_ERR_UNSUPPORTED, "2^23"),
+    (dict(batch=64, indices=FAKE, topk=1 << 23, block_table=0, cache_seqlens=0), m.MLA_ERR_UNSUPPORTED, "2^29"),
+    (dict(max_blocks_per_seq=(1 << 17) + 1), m.MLA_ERR_UNSUPPORTED, "2^17"),
 ]
 
 
@@ -162,6 +168,8 @@ def test_null_args_and_metadata_errors():
     assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 256, 0, FAKE, None) == m.MLA_ERR_INVALID
     assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 0, FAKE, FAKE, None) == m.MLA_ERR_INVALID
     assert b"num_parts" in L.mla_last_error()
+    assert L.mla_get_metadata(FAKE, 4, 1, 128, (1 << 23) + 1, 256, FAKE, FAKE, None) == m.MLA_ERR_UNSUPPORTED
+    assert b"2^23" in L.mla_last_error()
 
 
 QUANT_CASES = [
@@ -220,3 +228,4 @@ def test_absorb_entry_points_reject_bad_arguments(over, status, text):
 def test_absorb_rope_pointer_is_checked():
     assert m.lib().mla_absorb_q(FAKE, 0, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID
     assert m.lib().mla_absorb_q(FAKE, FAKE + 8, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID
+

@@ -95,3 +95,38 @@ def test_placement_spreads_work_over_xcds(seed):
         blk = busy[x * per:(x + 1) * per]
         assert not blk[k:].any()
     assert int(busy.sum()) <= used
+
+
+def test_coverage_checker_catches_planted_schedules():
+    """The GPU-side coverage checker (tests/test_gpu_metadata.py) rejects
+    schedules with a missing tile, a tile taken twice, a wrong split count
+    and a wrong split index, and accepts the reference schedule."""
+    import importlib.util
+    import os
+
+    spec = importlib.util.spec_from_file_location(
+        "gpu_meta", os.path.join(os.path.dirname(__file__), "test_gpu_metadata.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    check = mod.check_covers_every_tile_once
+    T = [5, 0, 3, 9, 1]
+    meta, off = split_schedule(T, 8, 2, 3)
+    check(meta, off, T)
+    live = [r for r in range(8) if meta[r, 5] == 0]
+    bad = meta.copy()
+    bad[live[0], 3] -= 1                     # a tile nobody takes
+    bad2 = meta.copy()
+    bad2[live[1], 1] = max(0, bad2[live[1], 1] - 1)   # a tile taken twice (or a gap elsewhere)
+    bad3 = off.copy()
+    bad3[1:] += 1                            # split counts off by one
+    bad4 = meta.copy()
+    bad4[live[1], 4] += 1                    # wrong first split index
+    for m, o in ((bad, off), (bad2, off), (meta, bad3), (bad4, off)):
+        with pytest.raises(AssertionError):
+            check(m, o, T)
+
+
+def test_lengths_past_the_longest_sequence_read_as_it():
+    """cache_seqlens entries above 2^23 tokens count 2^17 tiles (the
+    documented bound that keeps every schedule position below 2^31)."""
+    assert tile_counts([(1 << 23) + 5, (1 << 31) - 1, 1 << 23], 3, 1, 16, 0, 16) == [1 << 17] * 3
