@@ -15,7 +15,8 @@ import mla_latent_kv_10_amd as mla
 from oracle import mla_decode_ref
 from oracle.absorb import absorb_q, unabsorb_o
 
-from tests.gpu_helpers import compare, say
+from tests.gpu_helpers import compare, say, workload_floor_fn
+from workload.gen import Workload
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +128,10 @@ def test_absorbed_layer_end_to_end():
     o_ref, lse_ref = mla_decode_ref(q_bits.reshape(B, s_q, H, 576), _bits(kv).reshape(n_blocks, 64, 576).view(np.uint8)
                                     .reshape(n_blocks, 64, 1152), "bf16", block_table=bt.numpy(),
                                     cache_seqlens=seq.numpy(), softmax_scale=scale, causal=True)
-    compare(o, lse, o_ref, lse_ref, label="decode on the absorbed q")  # includes the empty row (L = 1, query 0)
+    w = Workload("decode on the absorbed q", q.cpu(), kv.view(torch.uint8).reshape(n_blocks, 64, 1152), "bf16", bt,
+                 seq, None, scale, True)
+    # includes the empty row (L = 1, query 0)
+    compare(o, lse, o_ref, lse_ref, label="decode on the absorbed q", floor_fn=workload_floor_fn(w))
     o_bits = _bits(o.cpu()).reshape(T, H, 512)
     u_ref = unabsorb_o(o_bits, _bits(w_uv))
     assert np.all(np.abs(out.float().cpu().numpy() - u_ref) <= _bound(o_bits, _bits(w_uv), u_ref, 512, False))

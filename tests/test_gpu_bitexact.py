@@ -159,3 +159,84 @@ def test_split_then_combine_equals_one_call(fmt, h_q, sparse):
     mla.mla_combine(a, side.cuda_stream)
     torch.cuda.synchronize()
     assert _same((o1, lse1), (o2, lse2))
+
+
+def _set_latent(flat, row, fmt):
+    """Overwrite the latent part of one cache row with large equal values
+    (bf16 20.0, or e4m3 code 0x7E = 448, its group's amax after scaling)."""
+    if fmt == "fp8":
+        flat[row, :512] = 0x7E
+    else:
+        flat[row, :1024].view(torch.int16)[:] = 0x41A0
+
+
+@pytest.mark.parametrize("fmt,h_q,causal", [("bf16", 128, False), ("bf16", 16, True), ("fp8", 128, True),
+                                            ("fp8", 64, False), ("bf16", 64, True)])
+def test_boundary_tokens(fmt, h_q, causal):
+    """For every query row (b, i): changing the last token it attends
+    (t = L_b - 1, or t = L_b - s_q + i when causal) changes o[b, i], and
+    changing the first token past its limit (a page-tail row, or the token the
+    next query position adds) leaves o[b, i] and lse[b, i] the same bit for
+    bit. The sequences end mid-page, on a page edge and one past it."""
+    say(f"boundary tokens {fmt} h_q={h_q} causal={causal}")
+    s_q = 2 if causal else 1
+    lens = [130, 128, 65]
+    w = make_workload(batch=3, s_q=s_q, h_q=h_q, seqlens=lens, kv_format=fmt, causal=causal, extra_blocks=3,
+                      seed=31)
+    base_kv = w.kv.clone()
+    base = run_gpu(w)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        for i in range(s_q):
+            last = L - s_q + i if causal else L - 1
+            for t, expect_change in ((last, True), (last + 1, False)):
+                page = int(w.block_table[b, t // 64]) if t // 64 < w.block_table.shape[1] else -1
+                if page < 0:
+                    continue  # no cache row holds position t (the sequence ends on a page edge)
+                kv = base_kv.clone()
+                _set_latent(kv.reshape(-1, kv.shape[2]), page * 64 + t % 64, fmt)
+                w.kv = kv
+                out = run_gpu(w)
+                torch.cuda.synchronize()
+                same = (torch.equal(_bits(out[0][b, i]), _bits(base[0][b, i]))
+                        and torch.equal(_bits(out[1][b, i]), _bits(base[1][b, i])))
+                assert same != expect_change, (b, i, t, expect_change)
+    w.kv = base_kv
+
+
+@pytest.mark.parametrize("fmt,h_q", [("bf16", 128), ("fp8", 16), ("bf16", 64)])
+def test_invalid_page_ids_inside_a_sequence(fmt, h_q):
+    """Block-table entries inside L that name no cache page (-1, or an id past
+    the pool) mask their 64 tokens: the result matches the oracle (whose
+    attended set skips them) and is the same bit for bit whichever invalid id
+    is used. Positions past the block table's row are masked too."""
+    from tests.gpu_helpers import compare, oracle, workload_floor_fn
+
+    say(f"invalid page ids {fmt} h_q={h_q}")
+    w = make_workload(batch=3, s_q=1, h_q=h_q, seqlens=[700, 300, 200], kv_format=fmt, extra_blocks=2, seed=32)
+    w.block_table[0, 2] = -1
+    w.block_table[0, 5] = w.num_blocks + 7
+    w.block_table[1, 0] = -1            # the first page of a sequence
+    w.block_table[2, 3] = -1            # its last, partly filled page
+    a = run_gpu(w)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle(w)
+    compare(a[0], a[1], o_ref, lse_ref, label="invalid page ids", floor_fn=workload_floor_fn(w))
+    w.block_table[0, 2] = 1 << 30
+    w.block_table[0, 5] = -5
+    w.block_table[1, 0] = w.num_blocks
+    w.block_table[2, 3] = -(1 << 30)
+    b_ = run_gpu(w)
+    torch.cuda.synchronize()
+    assert _same(a, b_)
+    # a block table of 3 pages: every sequence attends at most its first 192
+    # tokens, as if L were 192 (one part, so both runs split alike)
+    w.block_table = w.block_table[:, :3].contiguous()
+    c = run_gpu(w, num_parts=1)
+    torch.cuda.synchronize()
+    w.cache_seqlens = torch.tensor([192, 192, 192], dtype=torch.int32)
+    d = run_gpu(w, num_parts=1)
+    torch.cuda.synchronize()
+    assert _same(c, d)
+    o_ref, lse_ref = oracle(w)
+    compare(d[0], d[1], o_ref, lse_ref, label="positions past the block table", floor_fn=workload_floor_fn(w))

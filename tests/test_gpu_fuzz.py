@@ -12,7 +12,7 @@ import pytest
 
 from workload import make_workload
 
-from tests.gpu_helpers import compare, oracle, run_gpu, say
+from tests.gpu_helpers import compare, oracle, run_gpu, say, workload_floor_fn
 
 pytestmark = pytest.mark.gpu
 
@@ -51,4 +51,4 @@ def test_random_shapes_match_oracle(label, kw, num_parts):
     w = make_workload(name=label, **kw)
     o, lse, _, _ = run_gpu(w, num_parts=num_parts)
     o_ref, lse_ref = oracle(w)
-    compare(o, lse, o_ref, lse_ref, None, label)
+    compare(o, lse, o_ref, lse_ref, None, label, floor_fn=workload_floor_fn(w))

@@ -19,7 +19,7 @@ import torch
 import mla_latent_kv_10_amd as mla
 from workload import config_workload, make_workload
 
-from tests.gpu_helpers import compare, oracle, run_gpu, say
+from tests.gpu_helpers import compare, oracle, run_gpu, say, workload_floor_fn
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +106,7 @@ def test_graph_replays_match_eager(cfg, seqlen, rows):
         refs.append(outs[0])
 
     o_ref, lse_ref = oracle(w_b, rows)
-    compare(refs[1][0], refs[1][1], o_ref, lse_ref, rows, label=w_b.name)
+    compare(refs[1][0], refs[1][1], o_ref, lse_ref, rows, label=w_b.name, floor_fn=workload_floor_fn(w_b))
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):

@@ -9,7 +9,8 @@ import torch
 import mla_latent_kv_10_amd as mla
 from oracle import append_rows, mla_decode_ref, quantize_rows
 
-from tests.gpu_helpers import LSE_RTOL, O_TOL, say
+from tests.gpu_helpers import compare, say, workload_floor_fn
+from workload.gen import Workload
 
 pytestmark = pytest.mark.gpu
 
@@ -161,8 +162,6 @@ def test_written_cache_decodes_like_the_oracle():
     assert np.array_equal(kv.view(-1, 656).cpu().numpy(), cache)
     o_ref, lse_ref = mla_decode_ref(_bits(q), cache.reshape(n_blocks, 64, 656), "fp8", block_table=block_table.numpy(),
                                     cache_seqlens=seqlens.numpy(), softmax_scale=scale, causal=True)
-    do = np.abs(o.float().cpu().numpy() - o_ref).max()
-    lg = lse.cpu().numpy()
-    dl = (np.abs(lg - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()
-    say(f"  max|do| = {do:.3e}, max rel dlse = {dl:.3e}")
-    assert do <= O_TOL and dl <= LSE_RTOL
+    w = Workload("quantize then decode", q, torch.from_numpy(cache.reshape(n_blocks, 64, 656)), "fp8", block_table,
+                 seqlens, None, scale, True)
+    compare(o, lse, o_ref, lse_ref, label="quantize then decode", floor_fn=workload_floor_fn(w))
