@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """MLA decode throughput on one MI355X.
 
-A step is one pass of the whole decode path over one batch: the split
-schedule (metadata kernel), the split decode kernel, and the split merge
-(combine kernel). Steps run from a HIP graph over rotating copies of the
-inputs whose combined size exceeds 512 MB, so the 256 MB Infinity Cache does
-not serve the KV reads. Inputs are resident in HBM before timing starts.
+A step is one decode step of a 61-layer model over one batch, replayed as
+one HIP graph: the split schedule (metadata kernel) once, since every layer
+shares it, then per layer the split decode kernel and the split merge
+(combine kernel), each layer on its own copy of the inputs; the copies
+rotate over sets whose combined size exceeds 512 MB, so the 256 MB Infinity
+Cache does not serve the KV reads. Inputs are resident in HBM before timing
+starts. TFLOPS and GB/s count the 61 layers' work.
 
-Default workload: dense bf16 decode, B=16, s_q=1, h_q=128, sequence lengths
-drawn uniformly from [1024, 4096] (seed 0), 64-token pages with a shuffled
-block table. Prints one JSON line.
+Default run: the low-head workload (B=16, s_q=1, h_q=16, bf16, 64-token
+pages, shuffled block table) over sequence lengths 512 .. 65536; `value` is
+the TFLOPS at 65536. Beside it, each with its own roofline: dense bf16
+(h_q=128), FP8 causal (B=64, s_q=2, h_q=128, L=8192), sparse FP8 (topk
+2048), the sparse prefill chunk and the 64-head share. Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -360,13 +364,184 @@ def bench_absorb(args):
     print(json.dumps(out), flush=True)
 
 
+SWEEP_LENGTHS = (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)
+HEADLINE_L = 65536
+# (key, config number) of the workloads reported beside the sweep
+EXTRA_CONFIGS = (("dense_bf16_h128", 2), ("fp8_causal_h128", 4), ("sparse_fp8_h128", 5),
+                 ("sparse_prefill_bf16", 6), ("dense_bf16_h64", 7))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def roofline_entry(flops: int, kv_bytes: int, kernel_ms: float, traffic):
+    """The split kernel against its bound: HBM below the ridge (2.5 PFLOP/s / 8 TB/s), bf16 MFMA above."""
+    ai = flops / max(kv_bytes, 1)
+    if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        ach = kv_bytes / (kernel_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    else:
+        ach = flops / (kernel_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    r["traffic"] = traffic
+    r["kernel"] = "decode_kernel (mla_decode_splits)"
+    r["kernel_ms"] = round(kernel_ms, 5)
+    r["per_launch"] = {"flop": flops, "kv_bytes": kv_bytes}
+    return r
+
+
+LAYERS = 61  # layers of the model one decode step runs (the walkthrough's cache arithmetic, §五)
+
+
+def measure_decode(w, steps: int, warmup: int, num_parts: int, stream):
+    """Time one workload. Returns a dict of its figures.
+
+    A step is one decode step of a LAYERS-layer model on the whole batch, as
+    a serving loop replays it: the split schedule once (every layer shares
+    it: the lengths are the same), then per layer the split kernel and the
+    merge (mla_decode_with_kvcache), each layer on its own copy of q and the
+    cache. The copies rotate over input sets whose touched bytes exceed
+    512 MB (twice the Infinity Cache), all resident in HBM before timing.
+    Each of the `steps` timed steps is one replay of that step's HIP graph
+    between two events on the replay stream; ms_per_step is the median of the
+    per-replay times and value-style figures count LAYERS layers of work.
+    """
+    import ctypes
+    import statistics
+
+    import torch
+
+    import mla_latent_kv_10_amd as mla
+
+    dev = torch.device("cuda:0")
+    L = mla.lib()
+    pairs, kv_bytes = algorithmic_counts(w)
+    flops = pairs * FLOP_PER_PAIR
+    touched = kv_bytes + 2 * w.q.numel() * 2
+    n_sets = min(LAYERS, max(2, math.ceil(512e6 / max(touched, 1)) + 1))
+    base = {"q": w.q.to(dev), "kv": w.kv.to(dev),
+            "bt": None if w.block_table is None else w.block_table.to(dev),
+            "seq": w.cache_seqlens.to(dev),
+            "idx": None if w.indices is None else w.indices.to(dev)}
+    is_fp8 = w.kv_format == "fp8"
+    _, n_off = mla.metadata_size(w.batch, w.s_q, w.h_q, num_parts)
+    ws_bytes = mla.workspace_size(w.batch, w.s_q, w.h_q, num_parts)
+    tm = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+    so = torch.empty((n_off,), dtype=torch.int32, device=dev)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)  # layers run in order: one workspace
+    sets = []
+    for k in range(n_sets):
+        d = {key: (None if v is None else (v if k == 0 else v.clone())) for key, v in base.items()}
+        d["o"] = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+        d["lse"] = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+        d["args"] = mla.make_args(d["q"], d["kv"], d["bt"], d["seq"], tm, so, w.softmax_scale, w.causal,
+                                  is_fp8, d["idx"], ws, d["o"], d["lse"])
+        sets.append(d)
+    seq_ptr = 0 if w.indices is not None else sets[0]["seq"].data_ptr()
+
+    def metadata(s):
+        mla.check(L.mla_get_metadata(seq_ptr, w.batch, w.s_q, w.h_q, w.topk, num_parts, tm.data_ptr(),
+                                     so.data_ptr(), s))
+
+    def decode_step(s):
+        metadata(s)
+        for k in range(LAYERS):
+            mla.check(L.mla_decode_with_kvcache(ctypes.byref(sets[k % n_sets]["args"]), s))
+
+    with torch.cuda.stream(stream):
+        decode_step(stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        return g
+
+    def replay_timed(g, n, per):
+        """n replays, each between two events; per-replay ms / per."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        with torch.cuda.stream(stream):
+            ev[0].record(stream)
+            for k in range(n):
+                g.replay()
+                ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return [ev[k].elapsed_time(ev[k + 1]) / per for k in range(n)]
+
+    g_step = capture(decode_step)
+    # warm-up: W steps, then (bounded) until a replay is within 10 % of the
+    # best seen: memory that another workload freed just before can take a
+    # fraction of a second to reach full speed
+    seen = replay_timed(g_step, max(1, warmup), 1)
+    extra = 0
+    while seen[-1] > 1.1 * min(seen) and extra < 50:
+        seen += replay_timed(g_step, 1, 1)
+        extra += 1
+    t0 = time.perf_counter()
+    per_step = replay_timed(g_step, steps, 1)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = statistics.median(per_step)
+
+    # the split kernel alone (the dominant kernel): a graph of LAYERS launches
+    # over the input sets, replayed; its average launch duration
+    def splits_only(s):
+        for k in range(LAYERS):
+            mla.check(L.mla_decode_splits(ctypes.byref(sets[k % n_sets]["args"]), s))
+
+    g_dec = capture(splits_only)
+    reps = max(3, min(20, int(200.0 / max(ms, 1e-3))))
+    dec_ms = statistics.median(replay_timed(g_dec, reps, LAYERS))
+
+    def metadata_only(s):
+        for _ in range(LAYERS):
+            metadata(s)
+
+    g_meta = capture(metadata_only)
+    meta_ms = statistics.median(replay_timed(g_meta, 5, LAYERS))
+
+    traffic = measured_traffic(w.name, num_parts)
+    out = {
+        "workload": w.name,
+        "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "kv_format": w.kv_format, "causal": w.causal,
+        "topk": w.topk, "sum_seqlens": int(w.cache_seqlens.sum()),
+        "layers_per_step": LAYERS,
+        "ms_per_step": round(ms, 5),
+        "ms_per_step_mean": round(sum(per_step) / len(per_step), 5),
+        "ms_per_step_wall": round(wall_ms, 5),
+        "ms_per_layer": round(ms / LAYERS, 5),
+        "metadata_ms": round(meta_ms, 5),
+        "extra_warmup_steps": extra,
+        "tflops": round(LAYERS * flops / (ms * 1e-3) / 1e12, 3),
+        "kv_read_GBps": round(LAYERS * kv_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline_entry(flops, kv_bytes, dec_ms, traffic),
+        "rotating_input_sets": n_sets,
+        "flop_per_layer": flops, "kv_bytes_per_layer": kv_bytes,
+    }
+    del sets, g_step, g_dec, g_meta, base, tm, so, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..6 (default 2: dense bf16 h_q=128; 6: sparse prefill)")
-    ap.add_argument("--seqlen", type=int, default=65536, help="sequence length for workload 3")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=0,
+                    help="one workload only (1..7; 3 takes --seqlen); default: the length sweep of workload 3 "
+                         "with workloads 2, 4, 5, 6 and 7 beside it")
+    ap.add_argument("--seqlen", type=int, default=HEADLINE_L, help="sequence length for workload 3")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -388,169 +563,88 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe, max(1, args.steps))
         return
+    torch.cuda.set_device(0)
     if args.op == "quantize":
-        torch.cuda.set_device(0)
         bench_quantize(args)
         return
     if args.op == "absorb":
-        torch.cuda.set_device(0)
         bench_absorb(args)
         return
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    w = build_workload(args)
-    pairs, kv_bytes = algorithmic_counts(w)
-    flops = pairs * FLOP_PER_PAIR
     num_parts = args.num_parts or mla.default_num_parts(0)
+    stream = torch.cuda.Stream(device=torch.device("cuda:0"))
+    from workload import config_workload
 
-    # rotating input copies: touched bytes per step x sets > 512 MB
-    q_bytes = w.q.numel() * 2
-    touched = kv_bytes + 2 * q_bytes
-    n_sets = max(1, math.ceil(512e6 / max(touched, 1)) + 1)
-    sets = []
-    base = {
-        "q": w.q.to(dev), "kv": w.kv.to(dev),
-        "bt": None if w.block_table is None else w.block_table.to(dev),
-        "seq": w.cache_seqlens.to(dev),
-        "idx": None if w.indices is None else w.indices.to(dev),
-    }
-    is_fp8 = w.kv_format == "fp8"
-    n_meta, n_off = mla.metadata_size(w.batch, w.s_q, w.h_q, num_parts)
-    ws_bytes = mla.workspace_size(w.batch, w.s_q, w.h_q, num_parts)
-    for s in range(n_sets):
-        d = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
-        d["tm"] = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
-        d["so"] = torch.empty((n_off,), dtype=torch.int32, device=dev)
-        d["ws"] = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-        d["o"] = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
-        d["lse"] = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
-        d["args"] = mla.make_args(d["q"], d["kv"], d["bt"], d["seq"], d["tm"], d["so"], w.softmax_scale, w.causal,
-                                  is_fp8, d["idx"], d["ws"], d["o"], d["lse"])
-        sets.append(d)
-    L = mla.lib()
-    import ctypes
+    def progress(msg):
+        print(msg, file=sys.stderr, flush=True)
 
-    def step(d, stream):
-        sp = 0 if d["idx"] is not None else d["seq"].data_ptr()
-        mla.check(L.mla_get_metadata(sp, w.batch, w.s_q, w.h_q, w.topk, num_parts, d["tm"].data_ptr(),
-                                     d["so"].data_ptr(), stream))
-        mla.check(L.mla_decode_with_kvcache(ctypes.byref(d["args"]), stream))
-
-    stream = torch.cuda.Stream(device=dev)
-    G = n_sets * max(1, 64 // n_sets)  # steps per graph replay
-
-    def capture(n_steps):
-        g = torch.cuda.CUDAGraph()
-        # warm the path once outside capture
-        with torch.cuda.stream(stream):
-            for k in range(min(n_steps, n_sets)):
-                step(sets[k % n_sets], stream.cuda_stream)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for k in range(n_steps):
-                step(sets[k % n_sets], torch.cuda.current_stream().cuda_stream)
-        torch.cuda.synchronize()
-        return g
-
-    def run_steps(k_steps, full_g):
-        graphs = []
-        reps, rem = divmod(k_steps, G)
-        for _ in range(reps):
-            graphs.append(full_g)
-        if rem:
-            graphs.append(capture(rem))
-        return graphs
-
-    g_full = capture(G)
-    # warmup
-    with torch.cuda.stream(stream):
-        for gr in run_steps(args.warmup, g_full):
-            gr.replay()
-    torch.cuda.synchronize()
-    timed = run_steps(args.steps, g_full)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):  # graph replays launch on the current stream
-        e0.record(stream)
-        for gr in timed:
-            gr.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_ms_wall = (t1 - t0) * 1e3 / args.steps
-    step_ms = e0.elapsed_time(e1) / args.steps
-
-    # Split-kernel duration: a graph of mla_decode_splits launches alone (the
-    # metadata of each input set is already in place from the steps above),
-    # timed with events on the stream the graph launches on.
-    def capture_decode(n_launch):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for k in range(n_launch):
-                mla.check(L.mla_decode_splits(ctypes.byref(sets[k % n_sets]["args"]),
-                                              torch.cuda.current_stream().cuda_stream))
-        torch.cuda.synchronize()
-        return g
-
-    g_dec = capture_decode(G)
-    reps_dec = max(1, args.steps // G)
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        g_dec.replay()
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for _ in range(reps_dec):
-            g_dec.replay()
-        f1.record(stream)
-    torch.cuda.synchronize()
-    decode_ms = f0.elapsed_time(f1) / (reps_dec * G)
-
-    tflops = flops / (step_ms * 1e-3) / 1e12
-    kv_gbps_step = kv_bytes / (step_ms * 1e-3) / 1e9
-    kv_gbps_dec = kv_bytes / (decode_ms * 1e-3) / 1e9
-    ai = flops / max(kv_bytes, 1)
-    traffic = measured_traffic(w.name, num_parts)
-    if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
-        roof = {"bound": "hbm", "achieved": round(kv_gbps_dec, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(kv_gbps_dec / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    if args.config:
+        w = config_workload(args.config, seqlen=args.seqlen)
+        head = measure_decode(w, args.steps, args.warmup, num_parts, stream)
+        sweep, extras, cfg_desc = None, None, {"workload": w.name}
     else:
-        dec_tflops = flops / (decode_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    roof["kernel"] = "decode_kernel (mla_decode_splits)"
-    roof["kernel_ms"] = round(decode_ms, 5)
-    roof["per_launch"] = {"flop": flops, "kv_bytes": kv_bytes}
+        sweep = []
+        head = None
+        # the headline length first, on memory no earlier workload has used
+        for L_ in (HEADLINE_L,) + tuple(x for x in SWEEP_LENGTHS if x != HEADLINE_L):
+            w_ = config_workload(3, seqlen=L_)
+            r = measure_decode(w_, args.steps, args.warmup, num_parts, stream)
+            progress(f"sweep L={L_}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOPS, "
+                     f"split kernel {r['roofline']['frac']:.3f} of {r['roofline']['bound']}")
+            sweep.append({"L": L_, **{k: r[k] for k in ("ms_per_step", "ms_per_layer", "tflops", "kv_read_GBps",
+                                                         "metadata_ms", "extra_warmup_steps")},
+                          "roofline": r["roofline"]})
+            if L_ == HEADLINE_L:
+                head, w = r, w_
+            del w_
+        sweep.sort(key=lambda e: e["L"])
+        extras = {}
+        for key, cfg in EXTRA_CONFIGS:
+            w_ = config_workload(cfg)
+            r = measure_decode(w_, args.steps, args.warmup, num_parts, stream)
+            progress(f"{key}: {r['ms_per_step']} ms/step, {r['tflops']} TFLOPS, "
+                     f"split kernel {r['roofline']['frac']:.3f} of {r['roofline']['bound']}")
+            extras[key] = r
+            del w_
+        cfg_desc = {"workload": "low-head dense bf16 decode vs seqlen: B=16 s_q=1 h_q=16, L = "
+                                + ", ".join(str(x) for x in SWEEP_LENGTHS) + f"; value at L={HEADLINE_L}"}
 
     out = {
         "metric": METRIC,
-        "value": round(tflops, 3),
+        "value": head["tflops"],
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_format == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
+        "dtype": "bf16" if head["kv_format"] == "bf16" else "fp8-e4m3 cache, bf16 MFMA",
         "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
-            "kv_format": w.kv_format, "causal": w.causal, "topk": w.topk,
-            "sum_seqlens": int(w.cache_seqlens.sum()),
-            "num_parts": num_parts, "rotating_input_sets": n_sets, "graph_steps": G,
-        },
-        "kv_read_GBps": round(kv_gbps_step, 1),
-        "kv_read_frac_hbm": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
-        "tflops_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "ms_per_step_wall": round(step_ms_wall, 5),
+        "config": {**cfg_desc, "batch": head["batch"], "s_q": head["s_q"], "h_q": head["h_q"],
+                   "kv_format": head["kv_format"], "causal": head["causal"], "topk": head["topk"],
+                   "sum_seqlens": head["sum_seqlens"], "num_parts": num_parts,
+                   "rotating_input_sets": head["rotating_input_sets"],
+                   "step": f"one decode step of a {LAYERS}-layer model: the split schedule once, then per layer "
+                           "the split kernel and the merge on that layer's cache (one HIP graph replay)",
+                   "layers_per_step": LAYERS},
+        "kv_read_GBps": head["kv_read_GBps"],
+        "kv_read_frac_hbm": round(head["kv_read_GBps"] / HBM_PEAK_GBPS, 4),
+        "tflops_frac_bf16": round(head["tflops"] / BF16_PEAK_TFLOPS, 4),
+        "ms_per_step_mean": head["ms_per_step_mean"],
+        "ms_per_step_wall": head["ms_per_step_wall"],
+        "ms_per_layer": head["ms_per_layer"],
+        "metadata_ms": head["metadata_ms"],
         "kernel_source_hash": kernel_source_hash(),
-        "roofline": roof,
+        "roofline": head["roofline"],
     }
+    if sweep is not None:
+        out["sweep"] = sweep
+        out["configs"] = extras
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        cb = cpu_baseline(w, args.cpu_seconds)
+        cb["cpu_model"] = cpu_model()
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

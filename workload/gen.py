@@ -42,6 +42,7 @@ CONFIG_NAMES = {
     4: "fp8 paged causal: B=64 s_q=2 h_q=128 L=8192",
     5: "sparse fp8: B=32 s_q=1 h_q=128 topk=2048 (5% -1)",
     6: "sparse prefill bf16: B=1 s_q=1024 h_q=128 topk=2048 over a 32768-token prefix",
+    7: "dense bf16 64-head share: B=16 s_q=1 h_q=64 L~U[1024,4096]",
 }
 
 
@@ -215,7 +216,7 @@ def make_workload(
 
 
 def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
-    """The five decode workloads and the sparse prefill chunk (config 3 takes its fixed sequence length)."""
+    """The five decode workloads, the sparse prefill chunk (6) and the 64-head share (7); config 3 takes its fixed sequence length."""
     if cfg == 1:
         # q and cache drawn in fp32 then rounded to bf16; 4 pages, shuffled.
         return make_workload(batch=1, s_q=1, h_q=4, seqlens=[256], kv_format="bf16",
@@ -236,4 +237,9 @@ def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
     if cfg == 6:
         return make_workload(batch=1, s_q=1024, h_q=128, kv_format="bf16", topk=2048,
                              sparse_tokens_per_seq=32768, prefix_sparse=True, seed=seed, name=CONFIG_NAMES[6])
+    if cfg == 7:
+        # one GPU's share of 128 heads under two-way head sharding: the dense
+        # bf16 lengths with 64 heads (the 64-head row-group kernel)
+        return make_workload(batch=16, s_q=1, h_q=64, seqlen_range=(1024, 4096), kv_format="bf16",
+                             seed=seed, name=CONFIG_NAMES[7])
     raise ValueError(f"unknown config {cfg}")
