@@ -199,6 +199,26 @@ int mla_decode_splits(const mla_decode_args* args, void* stream);
 int mla_combine(const mla_decode_args* args, void* stream);
 
 /*
+ * mla_decode_with_kvcache without a caller workspace: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split workspace is the library's
+ * own static device array of MLA_STATIC_SCRATCH_BYTES, one per GPU, held
+ * until the process ends; this call allocates nothing (no hipMalloc, no
+ * allocating library routine). Same arguments, kernels and results as
+ * mla_decode_with_kvcache, except that args->workspace and
+ * args->workspace_bytes are ignored. The stream must belong to the current
+ * HIP device. No part of the scratch needs clearing: every slot the merge
+ * reads is written earlier in the same call. All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give wrong results; order them.
+ * Errors: those of mla_decode_with_kvcache, plus MLA_ERR_UNSUPPORTED when
+ * mla_workspace_size for the call shape exceeds MLA_STATIC_SCRATCH_BYTES
+ * (checked on the host before any HIP call).
+ */
+#define MLA_STATIC_SCRATCH_BYTES (64u << 20)
+int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream);
+
+/*
  * FP8 cache writer (quantise on write): turns n bf16 cache rows into the
  * 656-byte FP8 layout of [Guide] §"FP8 缓存怎么把 KV 压掉四成" and stores
  * row i at absolute cache row slots[i] (= page * 64 + offset, the row

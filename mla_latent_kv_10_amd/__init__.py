@@ -73,6 +73,7 @@ EXPORTS = (
     "mla_decode_with_kvcache",
     "mla_decode_splits",
     "mla_combine",
+    "mla_decode_with_kvcache_static",
     "mla_quantize_fp8_append",
     "mla_absorb_q",
     "mla_unabsorb_o",
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_with_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_decode_splits.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
+    L.mla_decode_with_kvcache_static.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.c_void_p]
     L.mla_quantize_fp8_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_int64, ctypes.c_void_p]
     L.mla_absorb_q.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
@@ -299,6 +301,11 @@ def mla_decode_with_kvcache(q, kv, block_table, cache_seqlens, head_dim_v: int, 
 def mla_decode_splits(args: MlaDecodeArgs, stream: int) -> None:
     """Run only the split kernel for a prepared argument block (mla_combine must follow)."""
     check(lib().mla_decode_splits(ctypes.byref(args), stream))
+
+
+def mla_decode_static(args: MlaDecodeArgs, stream: int) -> None:
+    """mla_decode_with_kvcache on the library's static scratch (allocates nothing; workspace fields ignored)."""
+    check(lib().mla_decode_with_kvcache_static(ctypes.byref(args), stream))
 
 
 def mla_combine(args: MlaDecodeArgs, stream: int) -> None:

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_common.h"
@@ -224,6 +225,80 @@ int mla_combine(const mla_decode_args* args, void* stream) {
     int st = prepare(args, &p);
     if (st) return st;
     hipError_t e = mla::launch_combine(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of mla_decode_with_kvcache_static: device memory of the library
+// itself, one copy on every GPU the library runs on, held until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels get the address hipGetSymbolAddress gives for the current
+// device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[MLA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream) {
+    if (!args) return fail(MLA_ERR_INVALID, "args is NULL");
+    if (args->struct_size != (int32_t)sizeof(mla_decode_args))
+        return fail(MLA_ERR_INVALID, "struct_size %d != sizeof(mla_decode_args) %d", args->struct_size,
+                    (int)sizeof(mla_decode_args));
+    int st = check_shape(args->batch, args->s_q, args->h_q, args->num_parts);
+    if (st) return st;
+    const size_t need = workspace_bytes(args->batch, args->s_q, args->h_q, args->num_parts);
+    if (need > (size_t)MLA_STATIC_SCRATCH_BYTES)
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of split workspace; the static scratch holds %zu "
+                    "(use mla_decode_with_kvcache with a workspace)",
+                    need, (size_t)MLA_STATIC_SCRATCH_BYTES);
+    // every other check, on the host, before any HIP call (the workspace
+    // fields of args are ignored: a placeholder stands in for the scratch)
+    mla_decode_args a = *args;
+    a.workspace = reinterpret_cast<void*>((uintptr_t)256);
+    a.workspace_bytes = MLA_STATIC_SCRATCH_BYTES;
+    mla::DecodeParams p;
+    st = prepare(&a, &p);
+    if (st) return st;
+    void* ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st) return st;
+    a.workspace = ptr;
+    st = prepare(&a, &p);
+    if (st) return st;
+    const mla::Layout l = mla::layout_for(a.h_q, a.s_q, a.batch, a.num_parts);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_decode(p, l.variant, a.kv_format == MLA_KV_FP8_656, a.indices != nullptr, s);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    e = mla::launch_combine(p, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -229,3 +229,23 @@ def test_absorb_rope_pointer_is_checked():
     assert m.lib().mla_absorb_q(FAKE, 0, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID
     assert m.lib().mla_absorb_q(FAKE, FAKE + 8, FAKE, 8, 16, FAKE, None) == m.MLA_ERR_INVALID
 
+
+@pytest.mark.parametrize("over,status,word", [c for c in CASES if not any(k.startswith("workspace") for k in c[0])])
+def test_static_entry_checks_arguments_first(over, status, word):
+    # every argument check runs on the host before the scratch is looked up
+    L = m.lib()
+    rc = L.mla_decode_with_kvcache_static(ctypes.byref(_args(**over)), None)
+    assert rc == status and word in L.mla_last_error().decode()
+
+
+def test_static_entry_refuses_shapes_beyond_its_scratch():
+    L = m.lib()
+    assert L.mla_decode_with_kvcache_static(None, None) == m.MLA_ERR_INVALID
+    # 1024 query positions x 128 heads: 1280 split slots of 128 KB, more than 64 MiB
+    a = _args(batch=1, s_q=1024, num_parts=256)
+    assert m.workspace_size(1, 1024, 128, 256) > 64 << 20
+    assert L.mla_decode_with_kvcache_static(ctypes.byref(a), None) == m.MLA_ERR_UNSUPPORTED
+    assert "static scratch" in L.mla_last_error().decode()
+    # the workspace fields are ignored: a NULL workspace is not the error reported
+    a = _args(workspace=0, workspace_bytes=0, batch=1, s_q=1024, num_parts=256)
+    assert L.mla_decode_with_kvcache_static(ctypes.byref(a), None) == m.MLA_ERR_UNSUPPORTED
