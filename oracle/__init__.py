@@ -13,6 +13,8 @@ the ``tests/test_oracle_*.py`` files. No function here is "parity unpinned".
 
 from .mla_oracle import (  # noqa: F401
     E4M3FN_VALUES,
+    FORMATS,
+    ue8m0_values,
     bf16_bits_to_f64,
     f32_to_bf16_bits,
     decode_rows,
@@ -22,5 +24,5 @@ from .mla_oracle import (  # noqa: F401
     lse_merge,
 )
 from .schedule import split_schedule, tile_counts  # noqa: F401
-from .quantize import f32_to_e4m3fn_codes, quantize_rows, append_rows  # noqa: F401
+from .quantize import f32_to_e4m3fn_codes, quantize_rows, append_rows, quantize_rows_528  # noqa: F401
 from .absorb import absorb_q, unabsorb_o  # noqa: F401

@@ -26,6 +26,13 @@ Readings where the pages are silent:
     the block table's row, is skipped in the same way;
   * FP8 rows dequantise as bf16_rne(fp32(code) * fp32(scale)), the product
     rounded once to fp32, then once to bf16.
+  * the 528-byte row ([Walkthrough] §八, the V4.1 format: 512 FP8 values and
+    16 UE8M0 scales, RoPE quantised too, data before scales; §十 lists
+    528 = 512 fp8 + 16 ue8m0) holds the whole 512-dim key: 448 latent dims,
+    then the 64 RoPE dims the other formats carry, so d_qk = 512 and the
+    value is the 448-dim latent; scale j (a byte e, value 2^(e - 127), 255 is
+    NaN) applies to values 32 j .. 32 j + 31, the block size that gives 16
+    scales for 512 values.
 """
 
 from __future__ import annotations
@@ -37,6 +44,14 @@ import numpy as np
 BLOCK_SIZE = 64
 D_QK = 576
 D_V = 512
+
+# Row formats: bytes per cached token, key dims (d_qk), value dims (d_v).
+FORMATS = {
+    "bf16": (1152, 576, 512),
+    "fp8": (656, 576, 512),
+    "fp8_528": (528, 512, 448),
+}
+MX_BLOCK = 32   # values per UE8M0 scale in the 528-byte row
 
 
 # --------------------------------------------------------------------------
@@ -85,16 +100,41 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 # Cache rows
 # --------------------------------------------------------------------------
 
+def ue8m0_values(e: np.ndarray) -> np.ndarray:
+    """UE8M0 scale bytes -> their values 2^(e - 127) as float32 (255 is NaN).
+
+    [Walkthrough] §三 (scale layout): a UE8M0 scale stores only a power of
+    two, an 8-bit exponent with no mantissa. e = 0 gives 2^-127, a float32
+    subnormal, still exact.
+    """
+    e = np.asarray(e, dtype=np.int64)
+    with np.errstate(over="ignore"):
+        v = np.ldexp(np.float64(1.0), e - 127).astype(np.float32)
+    return np.where(e == 255, np.float32(np.nan), v)
+
+
 def decode_rows(rows: np.ndarray, kv_format: str) -> np.ndarray:
-    """Raw cache rows (uint8 [n, row_bytes]) -> exact float64 values [n, 576].
+    """Raw cache rows (uint8 [n, row_bytes]) -> exact float64 values [n, d_qk].
 
     bf16 rows: 576 little-endian bf16 values (512 latent, then 64 rope).
     fp8 rows ([Guide] §"FP8 缓存怎么把 KV 压掉四成", §"容易踩的坑"): bytes
     [0, 512) are e4m3 codes for the latent, [512, 528) four little-endian fp32
     scales, one per 128 latent dims, [528, 656) the 64 rope values as bf16.
+    fp8_528 rows ([Walkthrough] §八, §九 "数据在前、scale 在后"): bytes
+    [0, 512) are e4m3 codes of all 512 key dims (448 latent, 64 rope), bytes
+    [512, 528) sixteen UE8M0 scales, scale j for dims 32 j .. 32 j + 31;
+    value = bf16_rne(fp32(code) * 2^(e - 127)), exact unless it leaves the
+    range of bf16.
     """
     rows = np.ascontiguousarray(rows, dtype=np.uint8)
     n = rows.shape[0]
+    if kv_format == "fp8_528":
+        assert rows.shape[1] == 528
+        code_vals = E4M3FN_VALUES[rows[:, :512]].astype(np.float32)
+        block_scale = np.repeat(ue8m0_values(rows[:, 512:528]), MX_BLOCK, axis=1)
+        with np.errstate(invalid="ignore", over="ignore", under="ignore"):
+            prod = code_vals * block_scale  # one fp32 rounding (exact within range)
+        return bf16_bits_to_f64(f32_to_bf16_bits(prod))
     if kv_format == "bf16":
         assert rows.shape[1] == 1152
         return bf16_bits_to_f64(rows.view("<u2").reshape(n, D_QK))
@@ -154,22 +194,22 @@ def attended_rows(
 # Attention
 # --------------------------------------------------------------------------
 
-def attend(q: np.ndarray, K: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Naive attention of h query rows against n keys; V = K[:, :512].
+def attend(q: np.ndarray, K: np.ndarray, scale: float, d_v: int = D_V) -> Tuple[np.ndarray, np.ndarray]:
+    """Naive attention of h query rows against n keys; V = K[:, :d_v] (the latent).
 
-    q: [h, 576] float64, K: [n, 576] float64. Returns o [h, 512], lse [h].
+    q: [h, d_qk] float64, K: [n, d_qk] float64. Returns o [h, d_v], lse [h].
     Scores are formed explicitly, then a two-pass softmax.
     """
     h = q.shape[0]
     n = K.shape[0]
     if n == 0:
-        return np.zeros((h, D_V)), np.full(h, -np.inf)
+        return np.zeros((h, d_v)), np.full(h, -np.inf)
     S = (q @ K.T) * scale                      # [h, n] explicit score matrix
     m = S.max(axis=1, keepdims=True)           # pass 1: row max
     E = np.exp(S - m)                          # pass 2: exponentials
     l = E.sum(axis=1, keepdims=True)
     P = E / l
-    o = P @ K[:, :D_V]
+    o = P @ K[:, :d_v]
     lse = (m + np.log(l))[:, 0]
     return o, lse
 
@@ -189,12 +229,14 @@ def mla_decode_ref(
 ) -> Tuple[np.ndarray, np.ndarray]:
     """Reference decode.
 
-    q: bf16 bit patterns uint16 [B, s_q, h_q, 576] (or float64 values).
+    q: bf16 bit patterns uint16 [B, s_q, h_q, d_qk] (or float64 values).
     kv: uint8 [num_blocks, 64, row_bytes] raw cache, or float64
-        [num_blocks*64, 576] already-decoded rows when kv_is_decoded.
+        [num_blocks*64, d_qk] already-decoded rows when kv_is_decoded.
+    kv_format: "bf16", "fp8" (d_qk 576, d_v 512) or "fp8_528" (d_qk 512,
+        d_v 448); with kv_is_decoded, d_v is 512 when d_qk is 576, else 448.
     softmax_scale is used as the float64 value of its float32 rounding.
     rows: optional subset of (b, i) pairs to evaluate (others left NaN).
-    Returns o float64 [B, s_q, h_q, 512] and lse float64 [B, s_q, h_q].
+    Returns o float64 [B, s_q, h_q, d_v] and lse float64 [B, s_q, h_q].
     """
     q = np.asarray(q)
     qv = bf16_bits_to_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
@@ -207,14 +249,18 @@ def mla_decode_ref(
     scale = float(np.float32(softmax_scale))
     if causal and indices is not None:
         raise ValueError("causal masking is defined for dense attention only")
-    o = np.full((B, s_q, h_q, D_V), np.nan)
+    d_qk = qv.shape[3]
+    d_v = FORMATS[kv_format][2] if not kv_is_decoded else (D_V if d_qk == D_QK else 448)
+    if not kv_is_decoded and d_qk != FORMATS[kv_format][1]:
+        raise ValueError(f"q has {d_qk} dims; a {kv_format} cache row has {FORMATS[kv_format][1]}")
+    o = np.full((B, s_q, h_q, d_v), np.nan)
     lse = np.full((B, s_q, h_q), np.nan)
     pairs = rows if rows is not None else [(b, i) for b in range(B) for i in range(s_q)]
     for b, i in pairs:
         r = attended_rows(b, i, s_q=s_q, num_rows=num_rows, block_table=block_table,
                           cache_seqlens=cache_seqlens, causal=causal, indices=indices)
         K = kv[r] if kv_is_decoded else decode_rows(flat[r], kv_format)
-        o[b, i], lse[b, i] = attend(qv[b, i], K, scale)
+        o[b, i], lse[b, i] = attend(qv[b, i], K, scale, d_v)
     return o, lse
 
 

@@ -105,3 +105,55 @@ def append_rows(cache_rows: np.ndarray, slots: np.ndarray, src_bf16_bits: np.nda
     ok = (slots >= 0) & (slots < out.shape[0])
     out[slots[ok]] = rows[ok]
     return out
+
+
+# --------------------------------------------------------------------------
+# The 528-byte row: 512 e4m3 codes + 16 UE8M0 scales
+# --------------------------------------------------------------------------
+#
+# [Walkthrough] §八 (the V4.1 format: 528 bytes per token, 512 FP8 values and
+# 16 UE8M0 scales, RoPE quantised too), §九 (data first, scales after) and §三
+# (a UE8M0 scale is a power of two with no mantissa, rounded *up* to a power
+# of two). Readings where the pages are silent:
+#   * the 512 values are the whole key row, 448 latent dims then 64 RoPE
+#     dims; scale j covers values 32 j .. 32 j + 31 (16 blocks of 32);
+#   * the scale of a block is the smallest power of two 2^k with
+#     448 * 2^k >= amax (2^0 for an all-zero block); its byte is k + 127,
+#     at least 0;
+#   * code = e4m3fn round-to-nearest-even of x / 2^k (exact division, at most
+#     448 in magnitude, so no clamp); signed zeros as for the 656-byte row.
+
+ROW_528 = 528
+D_528 = 512
+MX_BLOCK = 32
+
+
+def ue8m0_exponent_for(amax: np.ndarray) -> np.ndarray:
+    """Smallest k with 448 * 2^k >= amax, for amax > 0 (float32 values, exact).
+
+    With amax = f * 2^E, f in [0.5, 1) (frexp) and 448 = 0.875 * 2^9:
+    448 * 2^k >= amax  <=>  k >= E - 9 when f <= 0.875, else k >= E - 8.
+    """
+    f, E = np.frexp(np.asarray(amax, dtype=np.float64))
+    return (E - 9 + (f > 0.875)).astype(np.int64)
+
+
+def quantize_rows_528(src_bf16_bits: np.ndarray) -> np.ndarray:
+    """bf16 key rows [n, 512] (uint16 bit patterns: 448 latent, 64 RoPE) -> 528-byte rows [n, 528]."""
+    bits = np.asarray(src_bf16_bits, dtype=np.uint16)
+    if bits.ndim != 2 or bits.shape[1] != D_528:
+        raise ValueError("quantize_rows_528 takes bf16 rows of 512 values")
+    n = bits.shape[0]
+    x = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).reshape(n, D_528 // MX_BLOCK, MX_BLOCK)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_rows_528 takes finite values")
+    amax = np.abs(x).max(axis=2)
+    k = np.where(amax == 0, 0, ue8m0_exponent_for(np.where(amax == 0, 1.0, amax)))
+    e = np.maximum(k + 127, 0)
+    k = e - 127
+    y = np.ldexp(x.astype(np.float64), -k[:, :, None])      # exact: a power-of-two scaling
+    codes = f32_to_e4m3fn_codes(y.astype(np.float32)).reshape(n, D_528)
+    out = np.empty((n, ROW_528), dtype=np.uint8)
+    out[:, :D_528] = codes
+    out[:, D_528:] = e.astype(np.uint8)
+    return out

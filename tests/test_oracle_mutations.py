@@ -10,7 +10,7 @@ import tests.test_oracle_attention as ta
 import tests.test_oracle_formats as tf
 
 
-def _attend_no_rope(q, K, scale):
+def _attend_no_rope(q, K, scale, d_v=512):
     if K.shape[0] == 0:
         return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
     S = (q[:, :512] @ K[:, :512].T) * scale
@@ -20,7 +20,7 @@ def _attend_no_rope(q, K, scale):
     return (E / l) @ K[:, :512], (m + np.log(l))[:, 0]
 
 
-def _attend_wrong_value_slice(q, K, scale):
+def _attend_wrong_value_slice(q, K, scale, d_v=512):
     if K.shape[0] == 0:
         return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
     S = (q @ K.T) * scale
@@ -30,7 +30,7 @@ def _attend_wrong_value_slice(q, K, scale):
     return (E / l) @ K[:, 64:], (m + np.log(l))[:, 0]
 
 
-def _attend_lse_without_max(q, K, scale):
+def _attend_lse_without_max(q, K, scale, d_v=512):
     if K.shape[0] == 0:
         return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
     S = (q @ K.T) * scale
@@ -255,3 +255,93 @@ def test_absorb_mutants_are_caught(monkeypatch, mutant):
 def test_unabsorb_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(tab, "unabsorb_o", _unabsorb_reshaped_weights)
     assert any(_fails(p) for p in ABSORB_PINS)
+
+
+# ---- the 528-byte row -----------------------------------------------------
+
+import tests.test_oracle_528 as t528  # noqa: E402
+
+
+def _decode528_blocks_of_64(rows, kv_format):
+    if kv_format != "fp8_528":
+        return _real_decode(rows, kv_format)
+    rows = np.ascontiguousarray(rows)
+    vals = om.E4M3FN_VALUES[rows[:, :512]] * np.repeat(om.ue8m0_values(rows[:, 512:520]).astype(np.float64), 64, axis=1)
+    return vals
+
+
+def _decode528_bias_128(rows, kv_format):
+    if kv_format != "fp8_528":
+        return _real_decode(rows, kv_format)
+    rows = np.ascontiguousarray(rows)
+    return om.E4M3FN_VALUES[rows[:, :512]] * np.repeat(np.ldexp(1.0, rows[:, 512:].astype(np.int64) - 128), 32, axis=1)
+
+
+def _decode528_scales_reversed(rows, kv_format):
+    if kv_format != "fp8_528":
+        return _real_decode(rows, kv_format)
+    rows = np.array(rows, copy=True)
+    rows[:, 512:] = rows[:, 512:][:, ::-1]
+    return _real_decode(rows, kv_format)
+
+
+_real_attend = om.attend
+
+
+def _attend_value_from_the_end(q, K, scale, d_v=512):
+    o, lse = _real_attend(q, K, scale, K.shape[1])
+    return o[:, -d_v:], lse   # takes the last d_v dims (RoPE included) as the value
+
+
+import oracle.quantize as oq528  # noqa: E402
+
+_real_q528 = oq528.quantize_rows_528
+
+
+def _q528_scale_rounded_down(src):
+    out = _real_q528(src)
+    bits = np.asarray(src, dtype=np.uint16)
+    x = (bits.astype(np.uint32) << 16).view(np.float32).reshape(-1, 16, 32).astype(np.float64)
+    amax = np.abs(x).max(axis=2)
+    k = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0).astype(np.int64)
+    y = np.clip(np.ldexp(x, -k[:, :, None]), -448, 448).astype(np.float32)
+    out[:, :512] = oq528.f32_to_e4m3fn_codes(y).reshape(-1, 512)
+    out[:, 512:] = (k + 127).astype(np.uint8)
+    return out
+
+
+def _q528_blocks_of_16(src):
+    bits = np.asarray(src, dtype=np.uint16)
+    n = bits.shape[0]
+    x = (bits.astype(np.uint32) << 16).view(np.float32).reshape(n, 32, 16)
+    amax = np.abs(x).max(axis=2)
+    k = np.where(amax == 0, 0, oq528.ue8m0_exponent_for(np.where(amax == 0, 1.0, amax)))
+    y = np.ldexp(x.astype(np.float64), -k[:, :, None]).astype(np.float32)
+    out = np.empty((n, 528), dtype=np.uint8)
+    out[:, :512] = oq528.f32_to_e4m3fn_codes(y).reshape(n, 512)
+    out[:, 512:] = (k[:, ::2] + 127).astype(np.uint8)
+    return out
+
+
+PINS_528 = [t528.test_528_row_golden, t528.test_528_writer_golden, t528.test_528_round_trip_bound_and_generator_agreement,
+            t528.test_528_scale_is_the_smallest_power_of_two_covering_amax, t528.test_single_token_gives_its_448_latent_dims,
+            t528.test_absorbed_equals_unabsorbed_with_448_latent_dims]
+
+
+@pytest.mark.parametrize("mutant", [_decode528_blocks_of_64, _decode528_bias_128, _decode528_scales_reversed])
+def test_528_decode_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(om, "decode_rows", mutant)
+    monkeypatch.setattr(t528, "decode_rows", mutant)
+    assert any(_fails(p) for p in PINS_528)
+
+
+def test_528_value_slice_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(om, "attend", _attend_value_from_the_end)
+    monkeypatch.setattr(t528, "attend", _attend_value_from_the_end)
+    assert any(_fails(p) for p in PINS_528)
+
+
+@pytest.mark.parametrize("mutant", [_q528_scale_rounded_down, _q528_blocks_of_16])
+def test_528_writer_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(t528, "quantize_rows_528", mutant)
+    assert any(_fails(p) for p in PINS_528)

@@ -26,9 +26,13 @@ def test_page_facts():
         "64x512 fp32 output registers": 64 * 512 * 4 // 4,
         "decode FLOPs per (query row, token)": 2 * (om.D_QK + om.D_V),
         "decode bytes per token bf16": 2 * om.D_QK,
+        "fp8 528 row bytes": om.FORMATS["fp8_528"][1] * 1 + (om.FORMATS["fp8_528"][1] // om.MX_BLOCK) * 1,
+        "MLA 528 ratio to MHA": 65536 / 528,
     }
     for name, val in computed.items():
         f = facts[name]
         assert abs(val - f["value"]) <= f.get("tol", 0), (name, val, f)
-    assert ROW_BYTES == {"bf16": facts["bf16 row bytes"]["value"], "fp8": facts["fp8 row bytes"]["value"]}
+    assert ROW_BYTES == {"bf16": facts["bf16 row bytes"]["value"], "fp8": facts["fp8 row bytes"]["value"],
+                         "fp8_528": facts["fp8 528 row bytes"]["value"]}
+    assert {k: v[0] for k, v in om.FORMATS.items()} == ROW_BYTES
     assert om.D_QK == D_QK == 576 and om.D_V == D_V == 512 and om.BLOCK_SIZE == 64

@@ -16,5 +16,7 @@ from .gen import (  # noqa: F401
     make_workload,
     config_workload,
     quantize_fp8_656,
+    quantize_fp8_528,
+    QK_DIMS,
     CONFIG_NAMES,
 )

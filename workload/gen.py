@@ -31,7 +31,8 @@ BLOCK_SIZE = 64  # tokens per KV page (walkthrough §七 version table: paged KV
 D_QK = 576
 D_V = 512
 D_ROPE = 64
-ROW_BYTES = {"bf16": 1152, "fp8": 656}
+ROW_BYTES = {"bf16": 1152, "fp8": 656, "fp8_528": 528}
+QK_DIMS = {"bf16": 576, "fp8": 576, "fp8_528": 512}   # key (and query) dims per format
 FP8_GROUP = 128
 FP8_MAX = 448.0  # largest finite e4m3 magnitude (walkthrough §三 "为什么要量化")
 
@@ -118,6 +119,36 @@ def quantize_fp8_656(latent: torch.Tensor, rope_bf16: torch.Tensor) -> torch.Ten
     return out
 
 
+def quantize_fp8_528(x: torch.Tensor) -> torch.Tensor:
+    """Cache writer for the 528-byte row: fp32 key rows [N, 512] (448 latent,
+    then 64 RoPE) -> uint8 rows [N, 528].
+
+    Per block of 32 values: the scale is the smallest power of two 2^k with
+    448 * 2^k >= amax (2^0 for an all-zero block), stored as the byte k + 127
+    (UE8M0: walkthrough §三, scales rounded up to a power of two); code = e4m3
+    round-to-nearest-even of x / 2^k (exact; |x / 2^k| <= 448). Codes first,
+    the 16 scale bytes after (walkthrough §八, §九).
+    """
+    assert x.dtype == torch.float32 and x.shape[1] == 512
+    n = x.shape[0]
+    blocks = x.reshape(n, 16, 32)
+    amax = blocks.abs().amax(dim=2).to(torch.float64)
+    k = torch.zeros_like(amax, dtype=torch.int64)
+    nz = amax > 0
+    # smallest k with 448 * 2^k >= amax, searched from log2 and corrected exactly
+    k[nz] = torch.ceil(torch.log2(amax[nz] / 448.0)).to(torch.int64)
+    k[nz] += (torch.ldexp(torch.full_like(amax[nz], 448.0), k[nz]) < amax[nz]).to(torch.int64)
+    k[nz] -= (torch.ldexp(torch.full_like(amax[nz], 448.0), k[nz] - 1) >= amax[nz]).to(torch.int64)
+    e = torch.clamp(k + 127, min=0)
+    k = e - 127
+    y = torch.ldexp(blocks.to(torch.float64), -k.unsqueeze(2)).to(torch.float32)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, 512)
+    out = torch.empty((n, 528), dtype=torch.uint8)
+    out[:, :512] = codes
+    out[:, 512:] = e.to(torch.uint8)
+    return out
+
+
 def _cache_rows(gen: torch.Generator, n_rows: int, kv_format: str, chunk: int = 1 << 16) -> torch.Tensor:
     """n_rows cache rows drawn from N(0,1), in the requested byte layout (chunked to bound memory)."""
     rb = ROW_BYTES[kv_format]
@@ -126,6 +157,8 @@ def _cache_rows(gen: torch.Generator, n_rows: int, kv_format: str, chunk: int = 
         e = min(n_rows, s + chunk)
         if kv_format == "bf16":
             out[s:e] = _normal_bf16(gen, (e - s, D_QK)).view(torch.uint8).reshape(e - s, rb)
+        elif kv_format == "fp8_528":
+            out[s:e] = quantize_fp8_528(torch.randn(e - s, 512, generator=gen, dtype=torch.float32))
         else:
             latent = torch.randn(e - s, D_V, generator=gen, dtype=torch.float32)
             rope = _normal_bf16(gen, (e - s, D_ROPE))
@@ -178,7 +211,7 @@ def make_workload(
         else:
             seqlens_t = torch.tensor(list(seqlens), dtype=torch.int64)
         assert seqlens_t.numel() == batch
-        q = _normal_bf16(gen, (batch, s_q, h_q, D_QK))
+        q = _normal_bf16(gen, (batch, s_q, h_q, QK_DIMS[kv_format]))
         pages = [int(math.ceil(int(l) / BLOCK_SIZE)) for l in seqlens_t.tolist()]
         pool = sum(pages) + extra_blocks
         pool = max(pool, 1)
@@ -195,7 +228,7 @@ def make_workload(
     # sparse
     T = sparse_tokens_per_seq
     assert T % BLOCK_SIZE == 0 and topk <= T and not causal
-    q = _normal_bf16(gen, (batch, s_q, h_q, D_QK))
+    q = _normal_bf16(gen, (batch, s_q, h_q, QK_DIMS[kv_format]))
     n_blocks = batch * T // BLOCK_SIZE
     kv = _cache_rows(gen, n_blocks * BLOCK_SIZE, kv_format).reshape(n_blocks, BLOCK_SIZE, ROW_BYTES[kv_format])
     idx = torch.empty((batch, s_q, topk), dtype=torch.int32)
