@@ -30,6 +30,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FLOP_PER_PAIR = 2 * (576 + 512)  # QK^T over 576 dims + PV over 512 dims, per (query row, token)
+# per cache format: (bytes per cached token, FLOPs per (query row, token)); the
+# 528-byte rows hold 512-dim keys and 448-dim values
+FORMAT_COSTS = {"bf16": (1152, FLOP_PER_PAIR), "fp8": (656, FLOP_PER_PAIR), "fp8_528": (528, 2 * (512 + 448))}
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MLA decode TFLOPS and KV-read GB/s (% of MI355X roofline) vs seqlen, 1 GPU"
@@ -39,7 +42,7 @@ def algorithmic_counts(w):
     """(unmasked (row, token) pairs, KV bytes read once per sequence)."""
     import numpy as np
 
-    row_bytes = 1152 if w.kv_format == "bf16" else 656
+    row_bytes = FORMAT_COSTS[w.kv_format][0]
     if w.indices is not None:
         idx = w.indices.numpy()
         valid = (idx >= 0) & (idx < w.num_blocks * 64)
@@ -172,7 +175,7 @@ def cpu_baseline(w, seconds: float):
     dt = time.perf_counter() - t0
     threads = max([x.get("num_threads", 1) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
     return {
-        "value": done_pairs * FLOP_PER_PAIR / dt / 1e12,
+        "value": done_pairs * FORMAT_COSTS[w.kv_format][1] / dt / 1e12,
         "unit": "TFLOPS",
         "cores": int(threads),
         "kind": "oracle",
@@ -368,7 +371,8 @@ SWEEP_LENGTHS = (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)
 HEADLINE_L = 65536
 # (key, config number) of the workloads reported beside the sweep
 EXTRA_CONFIGS = (("dense_bf16_h128", 2), ("fp8_causal_h128", 4), ("sparse_fp8_h128", 5),
-                 ("sparse_prefill_bf16", 6), ("dense_bf16_h64", 7))
+                 ("sparse_prefill_bf16", 6), ("dense_bf16_h64", 7), ("fp8_528_causal_h128", 8),
+                 ("sparse_fp8_528_h128", 9))
 
 
 def cpu_model() -> str:
@@ -425,23 +429,24 @@ def measure_decode(w, steps: int, warmup: int, num_parts: int, stream):
     dev = torch.device("cuda:0")
     L = mla.lib()
     pairs, kv_bytes = algorithmic_counts(w)
-    flops = pairs * FLOP_PER_PAIR
+    flops = pairs * FORMAT_COSTS[w.kv_format][1]
     touched = kv_bytes + 2 * w.q.numel() * 2
     n_sets = min(LAYERS, max(2, math.ceil(512e6 / max(touched, 1)) + 1))
     base = {"q": w.q.to(dev), "kv": w.kv.to(dev),
             "bt": None if w.block_table is None else w.block_table.to(dev),
             "seq": w.cache_seqlens.to(dev),
             "idx": None if w.indices is None else w.indices.to(dev)}
-    is_fp8 = w.kv_format == "fp8"
+    is_fp8 = w.kv_format != "bf16"
     _, n_off = mla.metadata_size(w.batch, w.s_q, w.h_q, num_parts)
     ws_bytes = mla.workspace_size(w.batch, w.s_q, w.h_q, num_parts)
+    d_v = 448 if w.kv_format == "fp8_528" else 512
     tm = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
     so = torch.empty((n_off,), dtype=torch.int32, device=dev)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)  # layers run in order: one workspace
     sets = []
     for k in range(n_sets):
         d = {key: (None if v is None else (v if k == 0 else v.clone())) for key, v in base.items()}
-        d["o"] = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+        d["o"] = torch.empty((w.batch, w.s_q, w.h_q, d_v), dtype=torch.bfloat16, device=dev)
         d["lse"] = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
         d["args"] = mla.make_args(d["q"], d["kv"], d["bt"], d["seq"], tm, so, w.softmax_scale, w.causal,
                                   is_fp8, d["idx"], ws, d["o"], d["lse"])
@@ -539,8 +544,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=0,
-                    help="one workload only (1..7; 3 takes --seqlen); default: the length sweep of workload 3 "
-                         "with workloads 2, 4, 5, 6 and 7 beside it")
+                    help="one workload only (1..9; 3 takes --seqlen); default: the length sweep of workload 3 "
+                         "with workloads 2 and 4..9 beside it")
     ap.add_argument("--seqlen", type=int, default=HEADLINE_L, help="sequence length for workload 3")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

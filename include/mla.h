@@ -45,6 +45,13 @@ extern "C" {
 #define MLA_KV_BF16 0    /* 576 bf16 = 1152 B per token: latent 512, then rope 64 */
 #define MLA_KV_FP8_656 1 /* 656 B per token: 512 e4m3 latent codes, 4 fp32 scales
                             (one per 128 latent dims), 64 bf16 rope values */
+#define MLA_KV_FP8_528 2 /* 528 B per token ([Walkthrough] §八, the V4.1 row; §九 data
+                            before scales): 512 e4m3 codes of the whole key, 448
+                            latent dims then 64 rope dims, then 16 UE8M0 scale
+                            bytes, byte j scaling codes 32 j .. 32 j + 31 by
+                            2^(byte - 127). With this format the key (and q) has
+                            512 dims and the value (o) 448: q is
+                            [batch, s_q, h_q, 512], o is [batch, s_q, h_q, 448]. */
 
 #define MLA_BLOCK_SIZE 64 /* tokens per KV page */
 #define MLA_D_QK 576
@@ -132,15 +139,17 @@ typedef struct mla_decode_args {
     int32_t struct_size;       /* must equal sizeof(mla_decode_args) */
     int32_t batch, s_q, h_q;   /* num_heads_k is 1 ([Walkthrough] §六) */
     const void* q;             /* device bf16 [batch, s_q, h_q, 576]: absorbed latent
-                                  query (512) then rope query (64) */
+                                  query (512) then rope query (64); 512 dims (448 + 64)
+                                  with MLA_KV_FP8_528 */
     const void* kv;            /* device uint8 [num_blocks, 64, row_bytes] */
     int64_t num_blocks;        /* pages in the cache; num_blocks * 64 * row_bytes
                                   <= 2^32 (4 GiB: rows are addressed with 32-bit
                                   byte offsets from kv) */
     int32_t block_size;        /* must be 64 */
-    int32_t row_bytes;         /* 1152 for MLA_KV_BF16, 656 for MLA_KV_FP8_656; a
-                                  mismatch is rejected ([Guide] §"容易踩的坑") */
-    int32_t kv_format;         /* MLA_KV_BF16 or MLA_KV_FP8_656 */
+    int32_t row_bytes;         /* 1152 for MLA_KV_BF16, 656 for MLA_KV_FP8_656, 528 for
+                                  MLA_KV_FP8_528; a mismatch is rejected ([Guide]
+                                  §"容易踩的坑") */
+    int32_t kv_format;         /* MLA_KV_BF16, MLA_KV_FP8_656 or MLA_KV_FP8_528 */
     const int32_t* block_table;   /* dense: device int32 [batch, max_blocks_per_seq];
                                      token t of sequence b is row
                                      block_table[b, t/64]*64 + t%64 */
@@ -161,7 +170,8 @@ typedef struct mla_decode_args {
     int32_t num_parts;
     void* workspace;           /* device, >= mla_workspace_size bytes, 256-B aligned */
     size_t workspace_bytes;
-    void* o;                   /* device bf16 [batch, s_q, h_q, 512], written */
+    void* o;                   /* device bf16 [batch, s_q, h_q, 512] (448 with
+                                  MLA_KV_FP8_528), written */
     float* lse;                /* device fp32 [batch, s_q, h_q], written */
 } mla_decode_args;
 

@@ -30,7 +30,10 @@ MLA_ERR_WORKSPACE = -3
 MLA_ERR_HIP = -4
 MLA_KV_BF16 = 0
 MLA_KV_FP8_656 = 1
-ROW_BYTES = {MLA_KV_BF16: 1152, MLA_KV_FP8_656: 656}
+MLA_KV_FP8_528 = 2
+ROW_BYTES = {MLA_KV_BF16: 1152, MLA_KV_FP8_656: 656, MLA_KV_FP8_528: 528}
+# (key / query dims, value / output dims) per cache format
+DIMS = {MLA_KV_BF16: (576, 512), MLA_KV_FP8_656: (576, 512), MLA_KV_FP8_528: (512, 448)}
 
 
 class MlaDecodeArgs(ctypes.Structure):
@@ -180,6 +183,23 @@ def _expect(t, label: str, dtype, shape) -> None:
         raise ValueError(f"{label} must have shape [{want}] (got {list(t.shape)})")
 
 
+def cache_format(kv, is_fp8_kvcache: bool) -> int:
+    """The cache's row format: bf16 (576 bf16 values, or 1152 bytes), FP8 with
+    656-byte rows, or FP8 with 528-byte rows (both uint8 [num_blocks, 64, row])."""
+    torch = _torch()
+    if is_fp8_kvcache:
+        if kv is not None and kv.dtype == torch.uint8 and kv.dim() == 3 and kv.shape[2] == 528:
+            _expect(kv, "kv (FP8 cache, 528-byte rows)", torch.uint8, (None, 64, 528))
+            return MLA_KV_FP8_528
+        _expect(kv, "kv (FP8 cache: 656- or 528-byte rows)", torch.uint8, (None, 64, 656))
+        return MLA_KV_FP8_656
+    if kv is not None and kv.dtype == torch.bfloat16:
+        _expect(kv, "kv (bf16 cache)", torch.bfloat16, (None, 64, 576))
+    else:
+        _expect(kv, "kv (bf16 cache as bytes)", torch.uint8, (None, 64, 1152))
+    return MLA_KV_BF16
+
+
 def get_mla_metadata(cache_seqlens, s_q: int, h_q: int, topk: int = 0, num_parts: Optional[int] = None,
                      batch: Optional[int] = None):
     """Split schedule for one decode step; returns (tile_meta, split_offsets) int32 GPU tensors."""
@@ -210,6 +230,7 @@ def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softm
 
     q bf16 [B, s_q, h_q, 576]; kv [num_blocks, 64, 576] bf16 or [num_blocks,
     64, 1152] uint8 (bf16 cache), [num_blocks, 64, 656] uint8 (FP8 cache);
+    with an FP8 cache of 528-byte rows q has 512 dims and o 448;
     dense: block_table int32 [B, max_blocks_per_seq] and cache_seqlens int32
     [B]; sparse: indices int32 [B, s_q, topk]; tile_meta int32 [num_parts, 8]
     and split_offsets int32 [Q + 1] from get_mla_metadata for this (B, s_q,
@@ -218,14 +239,10 @@ def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softm
     Raises ValueError naming the first tensor that does not fit.
     """
     torch = _torch()
-    _expect(q, "q", torch.bfloat16, (None, None, None, 576))
+    fmt = cache_format(kv, is_fp8_kvcache)
+    d_qk, d_v = DIMS[fmt]
+    _expect(q, "q", torch.bfloat16, (None, None, None, d_qk))
     batch, s_q, h_q, _ = q.shape
-    if is_fp8_kvcache:
-        _expect(kv, "kv (FP8 cache)", torch.uint8, (None, 64, 656))
-    elif kv is not None and kv.dtype == torch.bfloat16:
-        _expect(kv, "kv (bf16 cache)", torch.bfloat16, (None, 64, 576))
-    else:
-        _expect(kv, "kv (bf16 cache as bytes)", torch.uint8, (None, 64, 1152))
     if indices is None:
         _expect(block_table, "block_table", torch.int32, (batch, None))
         _expect(cache_seqlens, "cache_seqlens", torch.int32, (batch,))
@@ -242,7 +259,7 @@ def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softm
         raise ValueError(f"metadata was built for (batch, s_q, h_q, topk) = {tuple(built)}, "
                          f"this call is {(batch, s_q, h_q, topk)}: call get_mla_metadata again")
     _expect(workspace, "workspace", torch.uint8, (None,))
-    _expect(o, "o", torch.bfloat16, (batch, s_q, h_q, 512))
+    _expect(o, "o", torch.bfloat16, (batch, s_q, h_q, d_v))
     _expect(lse, "lse", torch.float32, (batch, s_q, h_q))
     tensors = [q, kv, tile_meta, split_offsets, workspace, o, lse]
     tensors += [block_table, cache_seqlens] if indices is None else [indices]
@@ -256,7 +273,7 @@ def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softm
     a.num_blocks = kv.shape[0]
     a.block_size = kv.shape[1]
     a.row_bytes = kv[0, 0].numel() * kv.element_size()
-    a.kv_format = MLA_KV_FP8_656 if is_fp8_kvcache else MLA_KV_BF16
+    a.kv_format = fmt
     a.block_table = _ptr(block_table) if indices is None else 0
     a.max_blocks_per_seq = block_table.shape[1] if indices is None else 0
     a.cache_seqlens = _ptr(cache_seqlens) if indices is None else 0
@@ -275,11 +292,16 @@ def make_args(q, kv, block_table, cache_seqlens, tile_meta, split_offsets, softm
 def mla_decode_with_kvcache(q, kv, block_table, cache_seqlens, head_dim_v: int, tile_meta, split_offsets,
                             softmax_scale: Optional[float] = None, causal: bool = False,
                             is_fp8_kvcache: bool = False, indices=None, workspace=None, out=None):
-    """Decode attention; returns (o bf16 [B, s_q, h_q, 512], lse fp32 [B, s_q, h_q])."""
+    """Decode attention; returns (o bf16 [B, s_q, h_q, d_v], lse fp32 [B, s_q, h_q]).
+
+    d_v (head_dim_v) is 512, or 448 for an FP8 cache of 528-byte rows (whose q has 512 dims).
+    """
     torch = _torch()
-    if head_dim_v != 512:
-        raise ValueError("head_dim_v must be 512")
-    _expect(q, "q", torch.bfloat16, (None, None, None, 576))
+    fmt = cache_format(kv, is_fp8_kvcache)
+    d_qk, d_v = DIMS[fmt]
+    if head_dim_v != d_v:
+        raise ValueError(f"head_dim_v must be {d_v} for this cache format")
+    _expect(q, "q", torch.bfloat16, (None, None, None, d_qk))
     _expect(tile_meta, "tile_meta", torch.int32, (None, 8))
     batch, s_q, h_q, _ = q.shape
     if softmax_scale is None:
@@ -288,7 +310,7 @@ def mla_decode_with_kvcache(q, kv, block_table, cache_seqlens, head_dim_v: int, 
     if workspace is None:
         workspace = torch.empty((workspace_size(batch, s_q, h_q, num_parts),), dtype=torch.uint8, device=q.device)
     if out is None:
-        o = torch.empty((batch, s_q, h_q, 512), dtype=torch.bfloat16, device=q.device)
+        o = torch.empty((batch, s_q, h_q, d_v), dtype=torch.bfloat16, device=q.device)
         lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=q.device)
     else:
         o, lse = out

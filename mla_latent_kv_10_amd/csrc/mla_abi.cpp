@@ -65,12 +65,13 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (!aligned(a->q, 16) || !aligned(a->o, 16) || !aligned(a->kv, 16) || !aligned(a->lse, 4))
         return fail(MLA_ERR_INVALID, "q, o and kv must be 16-byte aligned, lse 4-byte aligned");
     if (a->block_size != mla::kBlock) return fail(MLA_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
-    if (a->kv_format != MLA_KV_BF16 && a->kv_format != MLA_KV_FP8_656)
+    if (a->kv_format != MLA_KV_BF16 && a->kv_format != MLA_KV_FP8_656 && a->kv_format != MLA_KV_FP8_528)
         return fail(MLA_ERR_INVALID, "unknown kv_format %d", a->kv_format);
-    const int want_row = a->kv_format == MLA_KV_BF16 ? 1152 : 656;
+    const int want_row = a->kv_format == MLA_KV_BF16 ? 1152 : (a->kv_format == MLA_KV_FP8_656 ? 656 : 528);
     if (a->row_bytes != want_row)
         return fail(MLA_ERR_INVALID, "row_bytes %d does not match kv_format %s (%d bytes per token)", a->row_bytes,
-                    a->kv_format == MLA_KV_BF16 ? "bf16" : "fp8-656", want_row);
+                    a->kv_format == MLA_KV_BF16 ? "bf16" : (a->kv_format == MLA_KV_FP8_656 ? "fp8-656" : "fp8-528"),
+                    want_row);
     if (a->num_blocks < 1) return fail(MLA_ERR_INVALID, "num_blocks must be >= 1");
     if (a->num_blocks * (int64_t)mla::kBlock >= ((int64_t)1 << 31))
         return fail(MLA_ERR_UNSUPPORTED, "num_blocks * 64 must be < 2^31");
@@ -202,9 +203,9 @@ int mla_decode_with_kvcache(const mla_decode_args* args, void* stream) {
     if (st) return st;
     const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format == MLA_KV_FP8_656, args->indices != nullptr, s);
+    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format, args->indices != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    e = mla::launch_combine(p, s);
+    e = mla::launch_combine(p, args->kv_format, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -214,7 +215,7 @@ int mla_decode_splits(const mla_decode_args* args, void* stream) {
     int st = prepare(args, &p);
     if (st) return st;
     const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
-    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format == MLA_KV_FP8_656, args->indices != nullptr,
+    hipError_t e = mla::launch_decode(p, l.variant, args->kv_format, args->indices != nullptr,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
@@ -224,7 +225,7 @@ int mla_combine(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = prepare(args, &p);
     if (st) return st;
-    hipError_t e = mla::launch_combine(p, static_cast<hipStream_t>(stream));
+    hipError_t e = mla::launch_combine(p, args->kv_format, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -296,9 +297,9 @@ int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream) {
     if (st) return st;
     const mla::Layout l = mla::layout_for(a.h_q, a.s_q, a.batch, a.num_parts);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = mla::launch_decode(p, l.variant, a.kv_format == MLA_KV_FP8_656, a.indices != nullptr, s);
+    hipError_t e = mla::launch_decode(p, l.variant, a.kv_format, a.indices != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    e = mla::launch_combine(p, s);
+    e = mla::launch_combine(p, a.kv_format, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ok();
 }

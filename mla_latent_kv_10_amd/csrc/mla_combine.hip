@@ -71,7 +71,10 @@ struct CombineMap {
 // split_offsets travels as a separate leading argument (the same pointer as
 // p.split_offsets), preloaded into SGPRs at dispatch, so the split-count
 // loads issue without waiting for the argument block.
-template <int RG, int VEC, int KU_MAX>
+// DV: value dims of o (512, or 448 for 528-byte rows). Slots always hold 512
+// dims per row; groups at dims >= DV are merged like the others (from slot
+// bytes the split kernel did not write) and never stored.
+template <int RG, int VEC, int KU_MAX, int DV>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ split_offsets, DecodeParams p) {
     using M = CombineMap<RG, VEC>;
     // XCD-aware numbering, as in the split kernel: the parts of one sequence
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     const int n = split_offsets[q + 1] - s0;
     if (n == 1) return;  // the split kernel wrote the final row
     const int64_t orow = ((int64_t)b * p.s_q + i) * p.h_q + h;
-    uint16_t* op = p.o + orow * kDv;
+    uint16_t* op = p.o + orow * DV;
     const bool lse_writer = dim[0] == 0;  // exactly one thread per row holds dim 0
     constexpr int kSlotBytes = RG * kDv * 2;  // fp16 partial rows of one slot
     float m = -INFINITY, s = 0.f;
@@ -179,20 +182,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
         i16x4 o4;
         #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = __builtin_bit_cast(short, (__bf16)(acc[j][e] * inv));
-        *(i16x4*)(op + dim[j]) = o4;
+        if (DV == kDv || dim[j] < DV) *(i16x4*)(op + dim[j]) = o4;
     }
     if (lse_writer) p.lse[orow] = empty ? -INFINITY : m + __logf(s);
 }
 
 }  // namespace
 
-template <int RG, int VEC, int KU_MAX>
+template <int RG, int VEC, int KU_MAX, int DV>
 void launch_map(const DecodeParams& p, int Q, hipStream_t s) {
-    hipLaunchKernelGGL((combine_kernel<RG, VEC, KU_MAX>), dim3((unsigned)Q * CombineMap<RG, VEC>::kBlocksPerQ), dim3(256),
-                       0, s, p.split_offsets, p);
+    hipLaunchKernelGGL((combine_kernel<RG, VEC, KU_MAX, DV>), dim3((unsigned)Q * CombineMap<RG, VEC>::kBlocksPerQ),
+                       dim3(256), 0, s, p.split_offsets, p);
 }
 
-hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
+template <int DV>
+void launch_dv(const DecodeParams& p, hipStream_t s) {
     const int Q = p.batch * p.n_rg;
     // At most one split per sequence on average (num_parts <= Q): most rows
     // were finished by the split kernel and the merge is mostly launch
@@ -202,14 +206,19 @@ hipError_t launch_combine(const DecodeParams& p, hipStream_t s) {
     // 21.4 -> 8.0 us; two splits per sequence: 11.6 -> 12.8 us, so not there).
     const bool wide = p.num_parts <= Q;
     if (p.rg == 128) {
-        if (wide) launch_map<128, 8, 4>(p, Q, s);
-        else launch_map<128, 2, 16>(p, Q, s);
+        if (wide) launch_map<128, 8, 4, DV>(p, Q, s);
+        else launch_map<128, 2, 16, DV>(p, Q, s);
     } else if (p.rg == 64) {
-        if (wide) launch_map<64, 8, 4>(p, Q, s);
-        else launch_map<64, 2, 16>(p, Q, s);
+        if (wide) launch_map<64, 8, 4, DV>(p, Q, s);
+        else launch_map<64, 2, 16, DV>(p, Q, s);
     } else {
-        launch_map<16, 2, 16>(p, Q, s);
+        launch_map<16, 2, 16, DV>(p, Q, s);
     }
+}
+
+hipError_t launch_combine(const DecodeParams& p, int format, hipStream_t s) {
+    if (format == kFmtFp8Mx) launch_dv<448>(p, s);
+    else launch_dv<kDv>(p, s);
     return hipGetLastError();
 }
 

@@ -28,6 +28,8 @@ constexpr int kMaxSeqTokens = 1 << 23;
 constexpr int kThreads = 256;       // four wave64s per workgroup
 
 enum Variant { kV128 = 0, kV16 = 1, kV64 = 2 };
+// Cache row formats (the kv_format values of include/mla.h).
+enum Format { kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp8Mx = 2 };
 
 // Row-group policy; it is part of the ABI contract (see include/mla.h).
 struct Layout {
@@ -84,7 +86,7 @@ struct DecodeParams {
 
 // Host-side launchers (defined in the .hip files).
 hipError_t launch_metadata(const MetaParams& p, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, int variant, bool fp8, bool sparse, hipStream_t s);
-hipError_t launch_combine(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int variant, int format, bool sparse, hipStream_t s);
+hipError_t launch_combine(const DecodeParams& p, int format, hipStream_t s);
 
 }  // namespace mla

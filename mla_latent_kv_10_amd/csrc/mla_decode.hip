@@ -45,9 +45,11 @@ using namespace dev;
 
 // ---------------------------------------------------------------- kernel
 
-template <bool FP8, bool SPARSE, int VAR>
+template <int FMT, bool SPARSE, int VAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
-    using S = Smem<FP8>;
+    using F = Fmt<FMT>;
+    using S = Smem<FMT>;
+    constexpr bool FP8 = F::kRaw;  // raw FP8 rows, dequantised in LDS
     // FP8 with 128-head groups spreads each tile's loads over the score MFMAs
     // of the tile two ahead (see the tile pipeline). Its bf16 tile and its two
     // raw tiles are separate LDS arrays; each raw array has a spare 1 KB after
@@ -65,9 +67,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // each tile wait for the next one's loads).
     constexpr bool kScalarIdx = !SPARSE;
     __shared__ __attribute__((aligned(1024))) char smem_raw[kFp8Pipe ? 1024 : S::kBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_tile[kFp8Pipe ? kTileBytes : 1024];
-    __shared__ __attribute__((aligned(1024))) char lds_raw0[kFp8Pipe ? kRawTileBytes + 1024 : 1024];
-    __shared__ __attribute__((aligned(1024))) char lds_raw1[kFp8Pipe ? kRawTileBytes + 1024 : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_tile[kFp8Pipe ? F::kTile : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw0[kFp8Pipe ? F::kRawTile + 1024 : 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw1[kFp8Pipe ? F::kRawTile + 1024 : 1024];
     // sparse index words of four tiles (tile x in slot x & 3), 64 per tile
     __shared__ __attribute__((aligned(256))) int32_t lds_ring[kFp8Pipe && SPARSE ? 4 * 64 : 1];
     char LDS_AS* smem = (char LDS_AS*)smem_raw;
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         const int so_raw = p.split_offsets[qq], so_end_raw = p.split_offsets[qq + 1];
 
         constexpr bool R32 = VAR != kV16;               // 32 rows per wave, 32x32x16 MFMA
-        constexpr int NQ = R32 ? 36 : 18;   // k-steps over 576 dims
+        constexpr int NQ = R32 ? F::kDqk / 16 : F::kDqk / 32;   // k-steps over the key dims
         bf16x8 qreg[NQ];
         {
             const int ln = opaque(lane);
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             // Rows past h_q (padding of the last row group) load head 0's q:
             // rows are independent and a padded row's output is never stored.
             const int h = sg.h0 + row;
-            const uint16_t* qbase = p.q + qrow0 * kDqk;           // head 0 of this query position
-            const int qoff = (h < p.h_q ? h : 0) * kDqk + dsub;   // this lane's row and sub-block
+            const uint16_t* qbase = p.q + qrow0 * F::kDqk;           // head 0 of this query position
+            const int qoff = (h < p.h_q ? h : 0) * F::kDqk + dsub;   // this lane's row and sub-block
             #pragma unroll
             for (int kk = 0; kk < NQ; ++kk) {
                 const int dim0 = R32 ? 16 * kk : 32 * kk;
@@ -255,12 +257,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     else row = dense_row(page0, n_valid, t);
                     if constexpr (UNROLL) {
                         #pragma unroll
-                        for (int ug = 0; ug < 9; ++ug)
-                            tile_load(dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                        for (int ug = 0; ug < F::kUg; ++ug)
+                            tile_load(dst + ((tg * F::kUg + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
                     } else {
                         #pragma unroll 1
-                        for (int ug = 0; ug < 9; ++ug)
-                            tile_load(dst + ((tg * 9 + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
+                        for (int ug = 0; ug < F::kUg; ++ug)
+                            tile_load(dst + ((tg * F::kUg + ug) << 10), row, (unsigned)(uu << 4), ug * 128);
                     }
                 };
                 if constexpr (UNROLL) {
@@ -271,52 +273,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     for (int g = 0; g < 2; ++g) group(g);
                 }
             } else {
-                // 41 chunks of the raw tile image, chunk c to wave c % 4.
-                // Chunk c holds 16-byte units kk = 64 c + lane of the image:
-                // token kk / 41, unit kk % 41. From chunk c to c + 4, kk grows by
-                // 256 = 6 * 41 + 10, so (token, unit) step without a division.
+                // kRawUnits (41 or 33) chunks of the raw tile image, chunk c
+                // to wave c % 4. Chunk c holds 16-byte units kk = 64 c + lane of
+                // the image: token kk / kRawUnits, unit kk % kRawUnits. From chunk
+                // c to c + 4, kk grows by 256 = kStepT * kRawUnits + kStepU, so
+                // (token, unit) step without a division.
+                constexpr int kStepT = 256 / F::kRawUnits, kStepU = 256 % F::kRawUnits;
                 const int kk0 = 64 * wave + opaque(lane);
-                int t = (kk0 * 1599) >> 16;  // kk0 / 41, exact for kk0 < 2624
-                int u = kk0 - t * kRawUnits;
+                int t = (int)(((unsigned)kk0 * F::kDivMagic) >> 16);  // kk0 / kRawUnits
+                int u = kk0 - t * F::kRawUnits;
                 auto chunk = [&](int c) {
                     unsigned row;
                     if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
                     else row = dense_row(page0, n_valid, t);
                     tile_load(dst + (c << 10), row, (unsigned)(u << 4), 0);
-                    u += 10;
-                    t += 6;
-                    if (u >= kRawUnits) { u -= kRawUnits; t += 1; }
+                    u += kStepU;
+                    t += kStepT;
+                    if (u >= F::kRawUnits) { u -= F::kRawUnits; t += 1; }
                 };
                 if constexpr (UNROLL) {
                     #pragma unroll
-                    for (int j = 0; j < 10; ++j) chunk(wave + 4 * j);
-                    if (wave == 0) chunk(40);
+                    for (int j = 0; j < F::kRawUnits / 4; ++j) chunk(wave + 4 * j);
+                    if (wave < F::kRawUnits % 4) chunk(wave + 4 * (F::kRawUnits / 4));
                 } else {
                     #pragma unroll 1
-                    for (int c = wave; c < kRawUnits; c += 4) chunk(c);
+                    for (int c = wave; c < F::kRawUnits; c += 4) chunk(c);
                 }
             }
             return mask;
         };
-        const int n_dma = FP8 ? (wave == 0 ? 11 : 10) : 18;
+        const int n_dma = FP8 ? (wave < F::kRawUnits % 4 ? F::kRawUnits / 4 + 1 : F::kRawUnits / 4) : 18;
 
-        // FP8, 128-head groups: chunk j (0..10) of a tile's raw image; chunk
-        // c = wave + 4 j holds 16-byte units kk = 64 c + lane (token kk / 41,
-        // unit kk % 41). Branch-free, so it can sit between MFMAs: waves 1..3
-        // have no chunk 10 and load nothing into the spare 1 KB after the tile
-        // instead, and a tile past the segment (no rows) loads nothing.
+        // FP8, 128-head groups: chunk slot j (0 .. kRawSlots - 1) of a tile's
+        // raw image; chunk c = wave + 4 j holds 16-byte units kk = 64 c + lane
+        // (token kk / kRawUnits, unit kk % kRawUnits). Branch-free, so it can
+        // sit between MFMAs: a wave whose last slot is past the image loads
+        // nothing into the spare 1 KB after the tile instead, and a tile past
+        // the segment (no rows) loads nothing.
         struct ChunkAddr {
             unsigned row, voff;
         };
         auto chunk_addr = [&](int j, const TileSrc& ts) -> ChunkAddr {
             const int c = wave + 4 * j;
             const int kk = 64 * c + (opaque(lane) & 63);
-            const int t = (int)(__umul24((unsigned)kk, 1599u) >> 16);  // kk / 41, exact for kk < 2624
-            const int u = kk - (int)__umul24((unsigned)t, (unsigned)kRawUnits);
+            const int t = (int)(__umul24((unsigned)kk, F::kDivMagic) >> 16);  // kk / kRawUnits
+            const int u = kk - (int)__umul24((unsigned)t, (unsigned)F::kRawUnits);
             unsigned row;
             if (SPARSE) {
                 // the chunk's 64 units span tokens tA .. tA + 2
-                const int tA = uniform((64 * c * 1599) >> 16);
+                const int tA = uniform((int)(((unsigned)(64 * c) * F::kDivMagic) >> 16));
                 const unsigned rA = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA, 63));
                 const unsigned rB = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA + 1, 63));
                 const unsigned rC = (unsigned)__builtin_amdgcn_readlane((int)ts.srow, min(tA + 2, 63));
@@ -324,24 +329,53 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             } else {
                 row = dense_row(ts.page0, ts.n_valid, t);
             }
-            return ChunkAddr{c < kRawUnits ? row : kOOB, (unsigned)(u << 4)};
+            return ChunkAddr{c < F::kRawUnits ? row : kOOB, (unsigned)(u << 4)};
         };
         auto chunk_issue = [&](int j, char LDS_AS* dst, const ChunkAddr& a) {
             const int c = wave + 4 * j;
-            dma16_asm(kv_words, lds_addr(dst + ((c < kRawUnits ? c : kRawUnits) << 10)), a.row, a.voff);
+            dma16_asm(kv_words, lds_addr(dst + ((c < F::kRawUnits ? c : F::kRawUnits) << 10)), a.row, a.voff);
         };
         auto raw_chunk = [&](int j, char LDS_AS* dst, const TileSrc& ts) { chunk_issue(j, dst, chunk_addr(j, ts)); };
 
         // Dequantise raw FP8 tile `raw` into the bf16 tile at `tile`. Lane l
-        // handles token l; wave w handles raw latent units w, w+4, .., w+28
-        // (16 codes each, scale group = unit / 8) and rope units w, w+4.
-        // All LDS reads are issued before any conversion.
+        // handles token l; wave w handles raw code units w, w+4, .., w+28
+        // (16 codes each; bf16 units 2u, 2u+1) and, for 656-byte rows, rope
+        // units w, w+4. All LDS reads are issued before any conversion.
         const int dq_x = (lane >> 1) & 7;  // swizzle of token `lane`
-        const int dq_base = ((lane >> 3) * 9 << 10) + ((lane & 7) << 7);
+        const int dq_base = ((lane >> 3) * F::kUg << 10) + ((lane & 7) << 7);
         const int dq_c0 = (((2 * wave) ^ dq_x) & 7) << 4;      // unit 2*(w+4j) & 7 == 2w
         const int dq_c1 = (((2 * wave + 1) ^ dq_x) & 7) << 4;
         auto dequant = [&](const char LDS_AS* raw, char LDS_AS* tile) {
-            const char LDS_AS* rrow = raw + lane * kRawRow;
+            const char LDS_AS* rrow = raw + lane * F::kRawRow;
+            if constexpr (F::kMx) {
+                // 528-byte rows: code unit u (values 16u .. 16u + 15) takes
+                // the UE8M0 scale byte 512 + u / 2 (blocks of 32 values). The
+                // scaled conversion multiplies by 2^(byte - 127) exactly: the
+                // fp32 operand's exponent field is the byte itself.
+                u32x4 c[8];
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) c[j] = *(const u32x4 LDS_AS*)(rrow + (wave + 4 * j) * 16);
+                const u32x4 e4 = *(const u32x4 LDS_AS*)(rrow + 512);
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int blk = 2 * j + (wave >> 1);               // (wave + 4 j) / 2
+                    const unsigned eb = (e4[j >> 1] >> (8 * (blk & 3))) & 0xFFu;
+                    const float sc = __uint_as_float(eb << 23);
+                    u32x4 w0, w1;
+                    #pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j][d], sc, false);
+                        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j][d], sc, true);
+                        const unsigned a = __builtin_bit_cast(unsigned, lo), b = __builtin_bit_cast(unsigned, hi);
+                        if (d < 2) { w0[2 * d] = a; w0[2 * d + 1] = b; }
+                        else { w1[2 * d - 4] = a; w1[2 * d - 3] = b; }
+                    }
+                    char LDS_AS* dst = tile + dq_base + (j << 10);
+                    *(u32x4 LDS_AS*)(dst + dq_c0) = w0;
+                    *(u32x4 LDS_AS*)(dst + dq_c1) = w1;
+                }
+                return;
+            }
             u32x4 c[8], rp[2];
             #pragma unroll
             for (int j = 0; j < 8; ++j) c[j] = *(const u32x4 LDS_AS*)(rrow + (wave + 4 * j) * 16);
@@ -378,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         constexpr int NB = (VAR == kV128) ? 2 : 1;      // 32-token blocks per wave per tile
         const int rw = (VAR == kV64) ? (wave >> 1) : wave;
         const int tw = (VAR == kV64) ? (wave & 1) : 0;
-        constexpr int NO = R32 ? 16 : 32;   // output blocks over 512 dims
+        constexpr int NO = R32 ? F::kDv / 32 : F::kDv / 16;   // output blocks over the value dims
         typedef typename std::conditional<R32, f32x16, f32x4>::type Acc;
         Acc oacc[NO];
         #pragma unroll
@@ -394,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
                 const int t = 32 * (VAR == kV128 ? blk : tw) + (lane & 31);
-                const int base = ((t >> 3) * 9 << 10) + ((t & 7) << 7);
+                const int base = ((t >> 3) * F::kUg << 10) + ((t & 7) << 7);
                 const int x = (t >> 1) & 7;
                 #pragma unroll
                 for (int j = 0; j < 4; ++j) koff[blk][j] = base + ((((2 * j + hh) ^ x) & 7) << 4);
@@ -415,21 +449,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             const int t = 16 * wave + (lane & 15);
             #pragma unroll
             for (int j = 0; j < 2; ++j)
-                koff[0][j] = ((t >> 3) * 9 << 10) + ((((t & 7) << 3) | (((4 * j + g) ^ ((t >> 1) & 7)) & 7)) << 4);
+                koff[0][j] = ((t >> 3) * F::kUg << 10) + ((((t & 7) << 3) | (((4 * j + g) ^ ((t >> 1) & 7)) & 7)) << 4);
             koff[1][0] = koff[1][1] = koff[1][2] = koff[1][3] = koff[0][2] = koff[0][3] = 0;
             const int r = (lane >> 2) & 3, c4 = lane & 3;
             const int tv = 16 * wave + 4 * g + r;
             #pragma unroll
             for (int dq = 0; dq < 4; ++dq) {
                 const int u7 = 2 * dq + (c4 >> 1);
-                voff[dq] = ((tv >> 3) * 9 << 10) + ((((tv & 7) << 3) | ((u7 ^ ((tv >> 1) & 7)) & 7)) << 4) + 8 * (c4 & 1);
+                voff[dq] = ((tv >> 3) * F::kUg << 10) + ((((tv & 7) << 3) | ((u7 ^ ((tv >> 1) & 7)) & 7)) << 4) + 8 * (c4 & 1);
             }
         }
 
         // ------------------------------------------------ compute one tile
         // Side work between the score MFMAs (tile loads; see the tile
-        // pipeline): side(j), j = 0..17, after the MFMAs of k-step 2 j (j < 17)
-        // or 33 (j = 17), when the tag is true.
+        // pipeline): side(j), j = 0 .. NQ/2 - 1, after the MFMAs of k-step 2 j
+        // (j < NQ/2 - 1) or NQ - 3 (the last j), when the tag is true.
         auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto side_tag, auto&& side) {
             constexpr bool kSideQk = decltype(side_tag)::value;
             if constexpr (R32) {
@@ -443,9 +477,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     #pragma unroll
                     for (int bb = 0; bb < NB; ++bb) ka[j][bb] = lds_read16(tile + koff[bb][j & 3] + ((j >> 2) << 10));
                 #pragma unroll
-                for (int kk = 0; kk < 36; ++kk) {
+                for (int kk = 0; kk < NQ; ++kk) {
                     const int nk = kk + kPF;
-                    if (nk < 36) {
+                    if (nk < NQ) {
                         #pragma unroll
                         for (int bb = 0; bb < NB; ++bb)
                             ka[nk % (kPF + 1)][bb] = lds_read16(tile + koff[bb][nk & 3] + ((nk >> 2) << 10));
@@ -456,18 +490,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                         sc[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % (kPF + 1)][bb], qreg[kk], sc[ch], 0, 0, 0);
                     }
                     if constexpr (kSideQk) {
-                        if (kk < 33 && kk % 2 == 0) side(kk / 2);
-                        else if (kk == 33) side(17);
+                        if (kk < NQ - 3 && kk % 2 == 0) side(kk / 2);
+                        else if (kk == NQ - 3) side(NQ / 2 - 1);
                     }
                 }
                 // keep the read-ahead: reads first, then (NB MFMA, NB reads) groups
                 __builtin_amdgcn_sched_group_barrier(0x100, NB * kPF, 0);
                 #pragma unroll
-                for (int kk = 0; kk < 36 - kPF; ++kk) {
+                for (int kk = 0; kk < NQ - kPF; ++kk) {
                     __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
                     if constexpr (kSideQk) {
-                        if ((kk < 33 && kk % 2 == 0) || kk == 33) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        if ((kk < NQ - 3 && kk % 2 == 0) || kk == NQ - 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                     }
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NB * kPF, 0);
@@ -505,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if (__builtin_amdgcn_ballot_w64(m_run != -INFINITY)) {
                         l_run *= alpha;
                         #pragma unroll
-                        for (int d = 0; d < 16; ++d) scale_agpr<f32x16, 16>(oacc[d], alpha);
+                        for (int d = 0; d < NO; ++d) scale_agpr<f32x16, 16>(oacc[d], alpha);
                         asm volatile("s_nop 2" ::: "memory");
                     }
                     m_run = m_new;
@@ -530,12 +564,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 // V operands (transposed reads) kVF MFMAs ahead; c = the tile's 16-token chunk
                 constexpr int kVF = 3;
-                constexpr int NPV = 32 * NB;
+                constexpr int NPV = NO * 2 * NB;   // (16-token chunk, 32-dim block) pairs
                 auto vread = [&](int n) -> bf16x8 {
-                    const int cl = n >> 4, d = n & 15;
+                    const int cl = n / NO, d = n % NO;
                     const int c = (VAR == kV128) ? cl : 2 * tw + cl;
-                    const i16x4 lo = lds_read_tr(tile + voff[d & 1] + (((2 * c) * 9 + (d >> 1)) << 10));
-                    const i16x4 hi = lds_read_tr(tile + voff[2 + (d & 1)] + (((2 * c + 1) * 9 + (d >> 1)) << 10));
+                    const i16x4 lo = lds_read_tr(tile + voff[d & 1] + (((2 * c) * F::kUg + (d >> 1)) << 10));
+                    const i16x4 hi = lds_read_tr(tile + voff[2 + (d & 1)] + (((2 * c + 1) * F::kUg + (d >> 1)) << 10));
                     const i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     return __builtin_bit_cast(bf16x8, av);
                 };
@@ -546,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int n = 0; n < NPV; ++n) {
                     if (n + kVF < NPV) va[(n + kVF) % (kVF + 1)] = vread(n + kVF);
-                    const int cl = n >> 4, d = n & 15;
+                    const int cl = n / NO, d = n % NO;
                     mfma32_agpr(oacc[d], va[n % (kVF + 1)], pb[cl]);
                 }
                 mfma_fence();  // MFMA results -> later AGPR reads / scaling
@@ -565,14 +599,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int j = 0; j < kPF; ++j) ka[j] = lds_read16(tile + koff[0][j & 1] + ((j >> 1) << 10));
                 #pragma unroll
-                for (int kk = 0; kk < 18; ++kk) {
+                for (int kk = 0; kk < NQ; ++kk) {
                     const int nk = kk + kPF;
-                    if (nk < 18) ka[nk % (kPF + 1)] = lds_read16(tile + koff[0][nk & 1] + ((nk >> 1) << 10));
+                    if (nk < NQ) ka[nk % (kPF + 1)] = lds_read16(tile + koff[0][nk & 1] + ((nk >> 1) << 10));
                     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk % (kPF + 1)], qreg[kk], s, 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, kPF, 0);
                 #pragma unroll
-                for (int kk = 0; kk < 18 - kPF; ++kk) {
+                for (int kk = 0; kk < NQ - kPF; ++kk) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
@@ -597,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     if (__builtin_amdgcn_ballot_w64(m_run != -INFINITY)) {
                         l_run *= alpha;
                         #pragma unroll
-                        for (int d = 0; d < 32; ++d) scale_agpr<f32x4, 4>(oacc[d], alpha);
+                        for (int d = 0; d < NO; ++d) scale_agpr<f32x4, 4>(oacc[d], alpha);
                         asm volatile("s_nop 2" ::: "memory");
                     }
                     m_run = m_new;
@@ -612,15 +646,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int j = 0; j < kVF; ++j) va[j] = lds_read_tr(tile + voff[j & 3] + ((j >> 2) << 10));
                 #pragma unroll
-                for (int d = 0; d < 32; ++d) {
-                    if (d + kVF < 32) va[(d + kVF) % (kVF + 1)] = lds_read_tr(tile + voff[(d + kVF) & 3] + (((d + kVF) >> 2) << 10));
+                for (int d = 0; d < NO; ++d) {
+                    if (d + kVF < NO) va[(d + kVF) % (kVF + 1)] = lds_read_tr(tile + voff[(d + kVF) & 3] + (((d + kVF) >> 2) << 10));
                     const i16x4 lo = va[d % (kVF + 1)];
                     const i16x8 av = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
                     oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[d], 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, kVF, 0);
                 #pragma unroll
-                for (int d = 0; d < 32 - kVF; ++d) {
+                for (int d = 0; d < NO - kVF; ++d) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
@@ -647,16 +681,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if constexpr (SPARSE) return (unsigned)lds_ring[(k & 3) * 64 + lane];
                 else return reg;
             };
-            if constexpr (SPARSE) wait_vm(36);  // the ring loads of t0..t0+2 (older than the split offsets and the 36 q loads)
+            if constexpr (SPARSE) wait_vm(NQ);  // the ring loads of t0..t0+2 (older than the split offsets and the NQ q loads)
             TileSrc ts = tile_src(t0, word_of(t0, idx_a));
             uint64_t mask_a = ts.mask, mask_b = 0;
             #pragma unroll
-            for (int j = 0; j < 11; ++j) raw_chunk(j, raw0, ts);
+            for (int j = 0; j < F::kRawSlots; ++j) raw_chunk(j, raw0, ts);
             if (t0 + 1 <= t1) {
                 ts = tile_src(t0 + 1, word_of(t0 + 1, idx_b));
                 mask_b = ts.mask;
                 #pragma unroll
-                for (int j = 0; j < 11; ++j) raw_chunk(j, raw1, ts);
+                for (int j = 0; j < F::kRawSlots; ++j) raw_chunk(j, raw1, ts);
             }
             // q was loaded before these tiles: have it in registers here. (The
             // compiler does not see the tile loads, so its wait for q also
@@ -669,27 +703,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 if constexpr (SPARSE) ring_load(k + 3);  // always issued: a fixed count per iteration
                 else idx_d = fetch_index(k + 3);
                 // VMEM instructions issued after tile k's loads: tile k + 1's
-                // (11; in the prologue only if that tile exists), and for the
-                // sparse index the ring loads of tiles k + 2 and k + 3 (dense
+                // (kRawSlots; in the prologue only if that tile exists), and for
+                // the sparse index the ring loads of tiles k + 2 and k + 3 (dense
                 // index words are scalar loads).
                 int after;
-                if (k == t0) after = (k + 1 <= t1 ? 11 : 0) + (SPARSE ? 1 : 0);
-                else after = 11 + (SPARSE ? 2 : 0);
+                if (k == t0) after = (k + 1 <= t1 ? F::kRawSlots : 0) + (SPARSE ? 1 : 0);
+                else after = F::kRawSlots + (SPARSE ? 2 : 0);
                 wait_vm(after);
                 block_sync_lds();
                 dequant(cur, tile);
                 block_sync_lds();
                 // sparse: the ring load of tile k + 2 (followed by tile k + 1's
                 // loads and the ring load of k + 3); at k = t0 it is already in
-                if (SPARSE && k > t0) wait_vm(12);
+                if (SPARSE && k > t0) wait_vm(F::kRawSlots + 1);
                 const TileSrc tn = (k + 2 <= t1) ? tile_src(k + 2, word_of(k + 2, idx_c)) : none;
                 // chunk j is issued with the address computed after chunk j - 1,
                 // so its VALU fills the MFMA slots between the two loads
                 ChunkAddr ca = chunk_addr(0, tn);
                 compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
-                    if (j < 11) {
+                    if (j < F::kRawSlots) {
                         chunk_issue(j, cur, ca);
-                        if (j + 1 < 11) ca = chunk_addr(j + 1, tn);
+                        if (j + 1 < F::kRawSlots) ca = chunk_addr(j + 1, tn);
                     }
                 });
                 idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
@@ -816,7 +850,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             float LDS_AS* xm = (float LDS_AS*)(smem + 2 * 16 * 4 * 64 * 16);  // [2][64] m, then [2][64] l
             if (tw == 1) {
                 #pragma unroll
-                for (int d = 0; d < 16; ++d)
+                for (int d = 0; d < NO; ++d)
                     #pragma unroll
                     for (int g = 0; g < 4; ++g)
                         *(f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4) =
@@ -831,7 +865,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const float e0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
                 const float e1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
                 #pragma unroll
-                for (int d = 0; d < 16; ++d)
+                for (int d = 0; d < NO; ++d)
                     #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 v = *(const f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4);
@@ -853,9 +887,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             const int hh = lane >> 5;
             if (final_out) {
                 if (h < p.h_q) {
-                    uint16_t* op = p.o + (qrow0 + h) * kDv;
+                    uint16_t* op = p.o + (qrow0 + h) * F::kDv;
                     #pragma unroll
-                    for (int d = 0; d < 16; ++d) {
+                    for (int d = 0; d < NO; ++d) {
                         #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             const int dim = 32 * d + 8 * g + 4 * hh;
@@ -873,15 +907,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // contiguous store per (d, g) per wave.
                 float amax = 0.f;
                 #pragma unroll
-                for (int d = 0; d < 16; ++d)
+                for (int d = 0; d < NO; ++d)
                     #pragma unroll
                     for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(oacc[d][v]));
                 amax = fmaxf(amax, wave_shfl_xor(amax, 32));
                 const unsigned ef = partial_exp_field(amax * inv);
                 const float sc = inv * exp_field_inv_pow2(ef);  // exact: inv times a power of two
+                // (a slot holds 512 dims per row whatever the value width)
                 f16x4* wp = (f16x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + lane;
                 #pragma unroll
-                for (int d = 0; d < 16; ++d) {
+                for (int d = 0; d < NO; ++d) {
                     #pragma unroll
                     for (int g = 0; g < 4; ++g)
                         wp[(d * 4 + g) * 64] = to_f16x4(oacc[d][4 * g] * sc, oacc[d][4 * g + 1] * sc,
@@ -906,11 +941,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             static_assert(4 * 16 * kMoStride * 4 + 2 * 64 * 4 <= S::kBytes, "merge buffers fit the tile area");
             const int row = lane & 15, g = lane >> 4;
             #pragma unroll
-            for (int d = 0; d < 32; ++d)
+            for (int d = 0; d < NO; ++d)
                 *(f32x4 LDS_AS*)(mo + (wave * 16 + row) * kMoStride + 16 * d + 4 * g) = oacc[d];
             if (g == 0) { mm[wave * 16 + row] = m_run; mm[64 + wave * 16 + row] = l_w; }
             block_sync_lds();
-            // thread -> row mr, dims 4c + 64j (j = 0..7): 16 threads cover 64 contiguous dims
+            // thread -> row mr, dims 4c + 64j (j < kDv / 64): 16 threads cover 64 contiguous dims
+            constexpr int NJ = F::kDv / 64;
             const int mr = tid >> 4;
             const int c4 = (tid & 15) * 4;
             float mw[4], lw[4];
@@ -923,20 +959,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             const float lse_v = l_tot > 0.f ? (mx + __log2f(l_tot)) * kLn2 : -INFINITY;
             const int h = sg.h0 + mr;
-            f32x4 acc[8];
+            f32x4 acc[NJ];
             #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const float ew = e[w] * inv;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * kMoStride + c4 + 64 * j);
+                for (int j = 0; j < NJ; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * kMoStride + c4 + 64 * j);
             }
             if (final_out) {
                 if (h < p.h_q) {
-                    uint16_t* op = p.o + (qrow0 + h) * kDv + c4;
+                    uint16_t* op = p.o + (qrow0 + h) * F::kDv + c4;
                     #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                    for (int j = 0; j < NJ; ++j) {
                         i16x4 w4;
                         #pragma unroll
                         for (int e2 = 0; e2 < 4; ++e2) w4[e2] = __builtin_bit_cast(short, (__bf16)acc[j][e2]);
@@ -949,16 +985,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // hold its 512 dims)
                 float amax = 0.f;
                 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < NJ; ++j)
                     #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) amax = fmaxf(amax, fabsf(acc[j][e2]));
                 #pragma unroll
                 for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, wave_shfl_xor(amax, m));
                 const unsigned ef = partial_exp_field(amax);
                 const float sc = exp_field_inv_pow2(ef);
-                uint16_t* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + c4;
+                uint16_t* wp = p.ws_o + ((int64_t)sg.slot * RG + mr) * kDv + c4;  // 512-dim slot rows
                 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < NJ; ++j)
                     *(f16x4*)(wp + 64 * j) = to_f16x4(acc[j][0] * sc, acc[j][1] * sc, acc[j][2] * sc, acc[j][3] * sc);
                 if ((tid & 15) == 0) {
                     p.ws_lse[(int64_t)sg.slot * RG + mr] = lse_v;
@@ -970,25 +1006,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     }
 }
 
-template <bool FP8, bool SPARSE, int VAR>
+template <int FMT, bool SPARSE, int VAR>
 hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<FP8, SPARSE, VAR>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((decode_kernel<FMT, SPARSE, VAR>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_format(const DecodeParams& p, int variant, bool sparse, hipStream_t s) {
+    if (variant == kV128) return sparse ? launch_one<FMT, true, kV128>(p, s) : launch_one<FMT, false, kV128>(p, s);
+    if (variant == kV64) return sparse ? launch_one<FMT, true, kV64>(p, s) : launch_one<FMT, false, kV64>(p, s);
+    return sparse ? launch_one<FMT, true, kV16>(p, s) : launch_one<FMT, false, kV16>(p, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int variant, bool fp8, bool sparse, hipStream_t s) {
-    if (variant == kV128) {
-        if (fp8) return sparse ? launch_one<true, true, kV128>(p, s) : launch_one<true, false, kV128>(p, s);
-        return sparse ? launch_one<false, true, kV128>(p, s) : launch_one<false, false, kV128>(p, s);
-    }
-    if (variant == kV64) {
-        if (fp8) return sparse ? launch_one<true, true, kV64>(p, s) : launch_one<true, false, kV64>(p, s);
-        return sparse ? launch_one<false, true, kV64>(p, s) : launch_one<false, false, kV64>(p, s);
-    }
-    if (fp8) return sparse ? launch_one<true, true, kV16>(p, s) : launch_one<true, false, kV16>(p, s);
-    return sparse ? launch_one<false, true, kV16>(p, s) : launch_one<false, false, kV16>(p, s);
+hipError_t launch_decode(const DecodeParams& p, int variant, int format, bool sparse, hipStream_t s) {
+    if (format == kFmtFp8) return launch_format<kFmtFp8>(p, variant, sparse, s);
+    if (format == kFmtFp8Mx) return launch_format<kFmtFp8Mx>(p, variant, sparse, s);
+    return launch_format<kFmtBf16>(p, variant, sparse, s);
 }
 
 }  // namespace mla

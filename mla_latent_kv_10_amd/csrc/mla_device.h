@@ -8,6 +8,7 @@ namespace dev {
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -19,22 +20,48 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;  // exponent reference moves when a row max grows by > 2^8
 constexpr unsigned kOOB = 0xFFFFFFFFu;
 
+// ---------------------------------------------------------------- cache row formats
+
+// What a cache row format fixes for the split kernel.
+//   bf16:     576 bf16 values (1152 B): 512 latent + 64 RoPE; the tile is used as loaded.
+//   fp8:      656 B: 512 e4m3 latent codes, 4 fp32 scales (one per 128), 64 bf16 RoPE.
+//   fp8_528:  528 B: 512 e4m3 codes (448 latent + 64 RoPE), 16 UE8M0 scales (one per 32).
+// Raw (FP8) rows land in LDS as stored and are dequantised into a bf16 tile of
+// kDqk values per token: kDqk / 8 16-byte units, grouped 8 to a 1 KB chunk
+// per 8 tokens (kUg unit groups per row).
+template <int FMT>
+struct Fmt {
+    static constexpr bool kRaw = FMT != kFmtBf16;
+    static constexpr bool kMx = FMT == kFmtFp8Mx;
+    static constexpr int kDqk = kMx ? 512 : 576;            // key and query dims
+    static constexpr int kDv = kMx ? 448 : 512;             // value (latent) dims
+    static constexpr int kUg = kDqk / 64;                   // unit groups per token group
+    static constexpr int kTile = kBlock * kDqk * 2;         // bf16 tile bytes in LDS
+    static constexpr int kRawRow = kMx ? 528 : 656;
+    static constexpr int kRawUnits = kRawRow / 16;          // 16-byte units per raw row (33, 41)
+    static constexpr int kRawTile = kBlock * kRawRow;       // kRawUnits KB
+    static constexpr int kRawSlots = (kRawUnits + 3) / 4;   // 1 KB chunk slots per wave per raw tile
+    // x * kDivMagic >> 16 == x / kRawUnits for 0 <= x < 64 * (kRawUnits + 1)
+    static constexpr unsigned kDivMagic = kMx ? 1986u : 1599u;
+};
+
 // ---------------------------------------------------------------- LDS layout
 
-template <bool FP8>
+template <int FMT>
 struct Smem {
     // bf16: two tiles (double buffer). FP8: two raw tiles + one bf16 tile.
+    using F = Fmt<FMT>;
     static constexpr int kTileA = 0;
-    static constexpr int kTileB = FP8 ? -1 : kTileBytes;
-    static constexpr int kRaw0 = FP8 ? kTileBytes : -1;
-    static constexpr int kRaw1 = FP8 ? kTileBytes + kRawTileBytes : -1;
-    static constexpr int kBytes = FP8 ? kTileBytes + 2 * kRawTileBytes : 2 * kTileBytes;
+    static constexpr int kTileB = F::kRaw ? -1 : F::kTile;
+    static constexpr int kRaw0 = F::kRaw ? F::kTile : -1;
+    static constexpr int kRaw1 = F::kRaw ? F::kTile + F::kRawTile : -1;
+    static constexpr int kBytes = F::kRaw ? F::kTile + 2 * F::kRawTile : 2 * F::kTile;
 };
 
 // ---------------------------------------------------------------- waits
 
 __device__ __forceinline__ void wait_vm(int n) {
-    // vmcnt takes an immediate; n is wave-uniform. Counts past the table wait for everything.
+    // vmcnt takes an immediate (0..63 on gfx950); n is wave-uniform. Counts past that wait for everything.
     switch (n) {
         case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
         case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
@@ -68,6 +95,38 @@ __device__ __forceinline__ void wait_vm(int n) {
         case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
         case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
         case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
+        case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+        case 33: asm volatile("s_waitcnt vmcnt(33)" ::: "memory"); break;
+        case 34: asm volatile("s_waitcnt vmcnt(34)" ::: "memory"); break;
+        case 35: asm volatile("s_waitcnt vmcnt(35)" ::: "memory"); break;
+        case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
+        case 37: asm volatile("s_waitcnt vmcnt(37)" ::: "memory"); break;
+        case 38: asm volatile("s_waitcnt vmcnt(38)" ::: "memory"); break;
+        case 39: asm volatile("s_waitcnt vmcnt(39)" ::: "memory"); break;
+        case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+        case 41: asm volatile("s_waitcnt vmcnt(41)" ::: "memory"); break;
+        case 42: asm volatile("s_waitcnt vmcnt(42)" ::: "memory"); break;
+        case 43: asm volatile("s_waitcnt vmcnt(43)" ::: "memory"); break;
+        case 44: asm volatile("s_waitcnt vmcnt(44)" ::: "memory"); break;
+        case 45: asm volatile("s_waitcnt vmcnt(45)" ::: "memory"); break;
+        case 46: asm volatile("s_waitcnt vmcnt(46)" ::: "memory"); break;
+        case 47: asm volatile("s_waitcnt vmcnt(47)" ::: "memory"); break;
+        case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+        case 49: asm volatile("s_waitcnt vmcnt(49)" ::: "memory"); break;
+        case 50: asm volatile("s_waitcnt vmcnt(50)" ::: "memory"); break;
+        case 51: asm volatile("s_waitcnt vmcnt(51)" ::: "memory"); break;
+        case 52: asm volatile("s_waitcnt vmcnt(52)" ::: "memory"); break;
+        case 53: asm volatile("s_waitcnt vmcnt(53)" ::: "memory"); break;
+        case 54: asm volatile("s_waitcnt vmcnt(54)" ::: "memory"); break;
+        case 55: asm volatile("s_waitcnt vmcnt(55)" ::: "memory"); break;
+        case 56: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
+        case 57: asm volatile("s_waitcnt vmcnt(57)" ::: "memory"); break;
+        case 58: asm volatile("s_waitcnt vmcnt(58)" ::: "memory"); break;
+        case 59: asm volatile("s_waitcnt vmcnt(59)" ::: "memory"); break;
+        case 60: asm volatile("s_waitcnt vmcnt(60)" ::: "memory"); break;
+        case 61: asm volatile("s_waitcnt vmcnt(61)" ::: "memory"); break;
+        case 62: asm volatile("s_waitcnt vmcnt(62)" ::: "memory"); break;
+        case 63: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 }

@@ -87,9 +87,10 @@ def run_gpu(w, g=None, num_parts: Optional[int] = None, device="cuda:0"):
         g = to_gpu(w, device)
     tm, so = mla.get_mla_metadata(g["cache_seqlens"] if w.indices is None else None, w.s_q, w.h_q,
                                   topk=w.topk, num_parts=num_parts, batch=w.batch)
-    o, lse = mla.mla_decode_with_kvcache(g["q"], g["kv"], g["block_table"], g["cache_seqlens"], 512, tm, so,
+    o, lse = mla.mla_decode_with_kvcache(g["q"], g["kv"], g["block_table"], g["cache_seqlens"],
+                                         448 if w.kv_format == "fp8_528" else 512, tm, so,
                                          softmax_scale=w.softmax_scale, causal=w.causal,
-                                         is_fp8_kvcache=(w.kv_format == "fp8"), indices=g["indices"])
+                                         is_fp8_kvcache=(w.kv_format != "bf16"), indices=g["indices"])
     return o, lse, tm, so
 
 
@@ -114,7 +115,7 @@ def oracle(w, rows: Optional[Iterable[Tuple[int, int]]] = None):
     seq = w.cache_seqlens.numpy()
     B, S = w.batch, w.s_q
     want = [(b, i) for b in range(B) for i in range(S)] if rows is None else list(rows)
-    o = np.full((B, S, w.h_q, 512), np.nan)
+    o = np.full((B, S, w.h_q, 448 if w.kv_format == "fp8_528" else 512), np.nan)
     lse = np.full((B, S, w.h_q), np.nan)
     by_b = {}
     for b, i in want:

@@ -22,7 +22,8 @@ def _same(a, b):
     return torch.equal(_bits(a[0]), _bits(b[0])) and torch.equal(_bits(a[1]), _bits(b[1]))
 
 
-@pytest.mark.parametrize("fmt,h_q", [("bf16", 128), ("bf16", 16), ("fp8", 128), ("fp8", 16)])
+@pytest.mark.parametrize("fmt,h_q", [("bf16", 128), ("bf16", 16), ("fp8", 128), ("fp8", 16), ("fp8_528", 128),
+                                     ("fp8_528", 16)])
 def test_page_shuffle_invariance(fmt, h_q):
     say(f"page shuffle {fmt} h_q={h_q}")
     w = make_workload(batch=3, s_q=1, h_q=h_q, seqlens=[700, 129, 64], kv_format=fmt, extra_blocks=5, seed=21)
@@ -38,7 +39,7 @@ def test_page_shuffle_invariance(fmt, h_q):
     assert _same(base, moved)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp8_528"])
 def test_gather_permutation_invariance(fmt):
     say(f"gather permutation {fmt}")
     w = make_workload(batch=2, s_q=1, h_q=128, kv_format=fmt, topk=300, sparse_tokens_per_seq=1024,
@@ -84,7 +85,8 @@ def _attended_rows(w):
 
 @pytest.mark.parametrize("fmt,h_q,causal,sparse", [("bf16", 128, False, False), ("bf16", 16, True, False),
                                                   ("fp8", 128, True, False), ("fp8", 16, False, False),
-                                                  ("fp8", 128, False, True), ("bf16", 16, False, True)])
+                                                  ("fp8", 128, False, True), ("bf16", 16, False, True),
+                                                  ("fp8_528", 128, True, False), ("fp8_528", 64, False, True)])
 def test_nan_poison_of_masked_rows(fmt, h_q, causal, sparse):
     """Every row no query attends to (page tails, causal-excluded tokens,
     unreferenced pages, rows named only by -1) is overwritten with NaN bytes;
@@ -116,7 +118,7 @@ def test_nan_poison_of_masked_rows(fmt, h_q, causal, sparse):
     # conversely, changing an attended boundary token changes the output
     last = keep[-1].item()
     bumped = nan.clone()
-    bumped[last, :64] = 0x3C if fmt == "fp8" else 0x40
+    bumped[last, :64] = 0x3C if fmt != "bf16" else 0x40
     w.kv = bumped.reshape(w.kv.shape)
     changed = run_gpu(w)
     torch.cuda.synchronize()
@@ -164,14 +166,15 @@ def test_split_then_combine_equals_one_call(fmt, h_q, sparse):
 def _set_latent(flat, row, fmt):
     """Overwrite the latent part of one cache row with large equal values
     (bf16 20.0, or e4m3 code 0x7E = 448, its group's amax after scaling)."""
-    if fmt == "fp8":
+    if fmt in ("fp8", "fp8_528"):
         flat[row, :512] = 0x7E
     else:
         flat[row, :1024].view(torch.int16)[:] = 0x41A0
 
 
 @pytest.mark.parametrize("fmt,h_q,causal", [("bf16", 128, False), ("bf16", 16, True), ("fp8", 128, True),
-                                            ("fp8", 64, False), ("bf16", 64, True)])
+                                            ("fp8", 64, False), ("bf16", 64, True), ("fp8_528", 128, True),
+                                            ("fp8_528", 16, False)])
 def test_boundary_tokens(fmt, h_q, causal):
     """For every query row (b, i): changing the last token it attends
     (t = L_b - 1, or t = L_b - s_q + i when causal) changes o[b, i], and

@@ -60,6 +60,22 @@ SMALL = [
                                                    sparse_tokens_per_seq=512, prefix_sparse=True)),
     ("fp8 sparse prefill chunk h16 s_q=33", dict(batch=1, s_q=33, h_q=16, kv_format="fp8", topk=100,
                                                  sparse_tokens_per_seq=256, prefix_sparse=True, invalid_frac=0.1)),
+    # 528-byte rows: 512-dim keys, 448-dim values, UE8M0 scales per 32 values
+    ("fp8_528 dense h128 ragged", dict(batch=3, s_q=1, h_q=128, seqlens=[1, 130, 700], kv_format="fp8_528")),
+    ("fp8_528 dense h16 ragged", dict(batch=4, s_q=1, h_q=16, seqlens=[64, 65, 1000, 3], kv_format="fp8_528")),
+    ("fp8_528 dense h64", dict(batch=3, s_q=1, h_q=64, seqlens=[1000, 1, 64], kv_format="fp8_528")),
+    ("fp8_528 causal s_q=2 h128", dict(batch=3, s_q=2, h_q=128, seqlens=[1000, 65, 1], kv_format="fp8_528",
+                                       causal=True)),
+    ("fp8_528 causal s_q=3 h20", dict(batch=2, s_q=3, h_q=20, seqlens=[300, 2], kv_format="fp8_528", causal=True)),
+    ("fp8_528 empty sequence h128", dict(batch=3, s_q=1, h_q=128, seqlens=[0, 100, 0], kv_format="fp8_528")),
+    ("fp8_528 sparse h128", dict(batch=3, s_q=1, h_q=128, kv_format="fp8_528", topk=200, sparse_tokens_per_seq=1024,
+                                 invalid_frac=0.05)),
+    ("fp8_528 sparse h128 s_q=2", dict(batch=3, s_q=2, h_q=128, kv_format="fp8_528", topk=130,
+                                       sparse_tokens_per_seq=704, invalid_frac=0.1)),
+    ("fp8_528 sparse h16 s_q=2", dict(batch=2, s_q=2, h_q=16, kv_format="fp8_528", topk=130,
+                                      sparse_tokens_per_seq=512, invalid_frac=0.1)),
+    ("fp8_528 sparse h64", dict(batch=2, s_q=1, h_q=64, kv_format="fp8_528", topk=300, sparse_tokens_per_seq=1024,
+                                invalid_frac=0.05)),
 ]
 
 
@@ -103,3 +119,15 @@ def test_config5_sparse_fp8_all_rows():
 
 def test_config6_sparse_prefill_all_rows():
     _check(config_workload(6), label="config 6 (sparse prefill, all rows)")
+
+
+def test_config7_64_head_share_all_rows():
+    _check(config_workload(7), label="config 7 (dense bf16, 64 heads, all rows)")
+
+
+def test_config8_fp8_528_causal_all_rows():
+    _check(config_workload(8), label="config 8 (528-byte rows, causal, all rows)")
+
+
+def test_config9_sparse_fp8_528_all_rows():
+    _check(config_workload(9), label="config 9 (528-byte rows, sparse, all rows)")

@@ -44,6 +44,8 @@ CONFIG_NAMES = {
     5: "sparse fp8: B=32 s_q=1 h_q=128 topk=2048 (5% -1)",
     6: "sparse prefill bf16: B=1 s_q=1024 h_q=128 topk=2048 over a 32768-token prefix",
     7: "dense bf16 64-head share: B=16 s_q=1 h_q=64 L~U[1024,4096]",
+    8: "fp8_528 paged causal: B=64 s_q=2 h_q=128 L=8192",
+    9: "sparse fp8_528: B=32 s_q=1 h_q=128 topk=2048 (5% -1)",
 }
 
 
@@ -249,7 +251,8 @@ def make_workload(
 
 
 def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
-    """The five decode workloads, the sparse prefill chunk (6) and the 64-head share (7); config 3 takes its fixed sequence length."""
+    """The five decode workloads, the sparse prefill chunk (6), the 64-head share (7) and the two FP8 shapes
+    with 528-byte rows (8, 9); config 3 takes its fixed sequence length."""
     if cfg == 1:
         # q and cache drawn in fp32 then rounded to bf16; 4 pages, shuffled.
         return make_workload(batch=1, s_q=1, h_q=4, seqlens=[256], kv_format="bf16",
@@ -275,4 +278,12 @@ def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
         # bf16 lengths with 64 heads (the 64-head row-group kernel)
         return make_workload(batch=16, s_q=1, h_q=64, seqlen_range=(1024, 4096), kv_format="bf16",
                              seed=seed, name=CONFIG_NAMES[7])
+    if cfg == 8:
+        # the FP8 causal shape with 528-byte rows (512 e4m3 codes, 16 UE8M0 scales)
+        return make_workload(batch=64, s_q=2, h_q=128, seqlens=[8192] * 64, kv_format="fp8_528",
+                             causal=True, seed=seed, name=CONFIG_NAMES[8])
+    if cfg == 9:
+        # the sparse FP8 shape with 528-byte rows
+        return make_workload(batch=32, s_q=1, h_q=128, kv_format="fp8_528", topk=2048,
+                             sparse_tokens_per_seq=32768, invalid_frac=0.05, seed=seed, name=CONFIG_NAMES[9])
     raise ValueError(f"unknown config {cfg}")
