@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = uniform(tid >> 6);
+    const int wave = uniform(tid >> 6) & 3;  // the & 3 tells the compiler the range (4 waves)
 
     // XCD-aware part numbering: hardware places workgroup x on XCD x % 8, so
     // consecutive logical parts (same sequence) share an XCD and its L2.
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             unsigned r = kOOB;
             if (k <= kmax) {
                 if (SPARSE) {
-                    const int pos = k * kBlock + lane;
+                    const int pos = k * kBlock + lane_fresh();
                     if (pos < p.topk) r = (unsigned)idx_row[pos];
                 } else if constexpr (kScalarIdx) {
                     // read-only for the whole kernel: a scalar load (lgkmcnt),
@@ -138,26 +138,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         const int ix_row0 = ((sg.b * p.s_q + sg.i) * p.topk);
         auto ring_load = [&](int k) {
             dma4_asm(ix_words, lds_addr((const char LDS_AS*)(lds_ring + (k & 3) * 64)),
-                     (unsigned)(ix_row0 + k * kBlock + (opaque(lane) & 63)) * 4u);
+                     (unsigned)(ix_row0 + k * kBlock + lane_fresh()) * 4u);
         };
         unsigned idx_a = kOOB, idx_b = kOOB, idx_c = kOOB;
         if constexpr (kFp8Pipe && SPARSE) {
             ring_load(t0);
             ring_load(t0 + 1);
             ring_load(t0 + 2);
+            // The wait before the first tile counts the VMEM loads issued
+            // after these three (the NQ q loads below): no later memory
+            // access may be moved above them.
+            asm volatile("" ::: "memory");
         } else {
             idx_a = load_index(t0, kmax0);
             idx_b = load_index(t0 + 1, kmax0);
             idx_c = load_index(t0 + 2, kmax0);
         }
-        const int len_raw = SPARSE ? 0 : p.seqlens[sg.b];
-        const int so_raw = p.split_offsets[qq], so_end_raw = p.split_offsets[qq + 1];
+        // read-only for the whole kernel: scalar loads (lgkmcnt), so that the
+        // wait for them does not also wait for the VMEM loads above
+        typedef const int32_t __attribute__((address_space(4))) cint32_t;
+        const int len_raw = SPARSE ? 0 : ((cint32_t*)p.seqlens)[sg.b];
+        const int so_raw = ((cint32_t*)p.split_offsets)[qq], so_end_raw = ((cint32_t*)p.split_offsets)[qq + 1];
 
         constexpr bool R32 = VAR != kV16;               // 32 rows per wave, 32x32x16 MFMA
         constexpr int NQ = R32 ? F::kDqk / 16 : F::kDqk / 32;   // k-steps over the key dims
         bf16x8 qreg[NQ];
         {
-            const int ln = opaque(lane);
+            const int ln = lane_fresh();
             int row, dsub;
             if constexpr (R32) { row = 32 * ((VAR == kV64) ? (wave >> 1) : wave) + (ln & 31); dsub = 8 * (ln >> 5); }
             else { row = ln & 15; dsub = 8 * (ln >> 4); }
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 ts.mask = (ts.page0 < 0 || ts.n_valid <= 0) ? 0ull
                           : (ts.n_valid >= 64 ? ~0ull : ((1ull << ts.n_valid) - 1ull));
             } else {
-                const bool in_row = k * kBlock + lane < p.topk;  // ring words past topk belong to other rows
+                const bool in_row = k * kBlock + lane_fresh() < p.topk;  // ring words past topk belong to other rows
                 ts.srow = (in_row && (int)word >= 0 && (int)word < p.num_rows) ? word : kOOB;  // -1, out of range
                 ts.mask = __builtin_amdgcn_ballot_w64(ts.srow != kOOB);
             }
@@ -243,13 +250,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             const int page0 = ts.page0, n_valid = ts.n_valid;
             const unsigned srow = ts.srow;
             const uint64_t mask = ts.mask;
+            const int w = opaque_s(wave) & 3;  // chunk geometry computed per tile, not held across the loop
             if (!FP8) {
                 // 72 chunks, 18 per wave: token groups 2w, 2w+1; unit groups 0..8.
                 auto group = [&](int g) {
                     // lane geometry recomputed here (not hoisted and spilled: a
                     // scratch reload would make the issue wait for q)
-                    const int ln = opaque(lane);
-                    const int tg = 2 * wave + g;
+                    const int ln = lane_fresh();
+                    const int tg = 2 * w + g;
                     const int t = tg * 8 + (ln >> 3);
                     const int uu = (ln & 7) ^ ((t >> 1) & 7);
                     unsigned row;
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // c to c + 4, kk grows by 256 = kStepT * kRawUnits + kStepU, so
                 // (token, unit) step without a division.
                 constexpr int kStepT = 256 / F::kRawUnits, kStepU = 256 % F::kRawUnits;
-                const int kk0 = 64 * wave + opaque(lane);
+                const int kk0 = 64 * w + lane_fresh();
                 int t = (int)(((unsigned)kk0 * F::kDivMagic) >> 16);  // kk0 / kRawUnits
                 int u = kk0 - t * F::kRawUnits;
                 auto chunk = [&](int c) {
@@ -293,11 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 };
                 if constexpr (UNROLL) {
                     #pragma unroll
-                    for (int j = 0; j < F::kRawUnits / 4; ++j) chunk(wave + 4 * j);
-                    if (wave < F::kRawUnits % 4) chunk(wave + 4 * (F::kRawUnits / 4));
+                    for (int j = 0; j < F::kRawUnits / 4; ++j) chunk(w + 4 * j);
+                    if (w < F::kRawUnits % 4) chunk(w + 4 * (F::kRawUnits / 4));
                 } else {
                     #pragma unroll 1
-                    for (int c = wave; c < F::kRawUnits; c += 4) chunk(c);
+                    for (int c = w; c < F::kRawUnits; c += 4) chunk(c);
                 }
             }
             return mask;
@@ -314,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             unsigned row, voff;
         };
         auto chunk_addr = [&](int j, const TileSrc& ts) -> ChunkAddr {
-            const int c = wave + 4 * j;
-            const int kk = 64 * c + (opaque(lane) & 63);
+            const int c = (opaque_s(wave) & 3) + 4 * j;
+            const int kk = 64 * c + lane_fresh();
             const int t = (int)(__umul24((unsigned)kk, F::kDivMagic) >> 16);  // kk / kRawUnits
             const int u = kk - (int)__umul24((unsigned)t, (unsigned)F::kRawUnits);
             unsigned row;
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             return ChunkAddr{c < F::kRawUnits ? row : kOOB, (unsigned)(u << 4)};
         };
         auto chunk_issue = [&](int j, char LDS_AS* dst, const ChunkAddr& a) {
-            const int c = wave + 4 * j;
+            const int c = (opaque_s(wave) & 3) + 4 * j;
             dma16_asm(kv_words, lds_addr(dst + ((c < F::kRawUnits ? c : F::kRawUnits) << 10)), a.row, a.voff);
         };
         auto raw_chunk = [&](int j, char LDS_AS* dst, const TileSrc& ts) { chunk_issue(j, dst, chunk_addr(j, ts)); };
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     #pragma unroll
                     for (int v = 0; v < 16; ++v) sc[bb][v] *= p.scale_log2;
                 if (mask != ~0ull) {
-                    const uint64_t mh = mask >> (4 * hh);
+                    const uint64_t mh = mask >> (4 * (lane_fresh() >> 5));  // this lane's token half
                     #pragma unroll
                     for (int bb = 0; bb < NB; ++bb) {
                         const int tb = (VAR == kV128) ? bb : tw;
@@ -743,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             char LDS_AS* buf1 = smem + S::kTileB;
             const TileSrc none{-1, 0, kOOB, 0ull};
             // lane geometry of this wave's chunks: token groups tg = 2w + g
-            const int ln = opaque(lane) & 63;
+            const int ln = lane_fresh();
             int trow[2], uu16[2];
             #pragma unroll
             for (int g = 0; g < 2; ++g) {
@@ -754,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             // chunk j of a tile: token group g = j / 9, unit group ug = j % 9
             auto qk_chunk = [&](int j, char LDS_AS* dst, const unsigned (&rows)[2]) {
                 const int g = j / 9, ug = j % 9;
-                dma16_asm(kv_words, lds_addr(dst + (((2 * wave + g) * 9 + ug) << 10)), rows[g], (unsigned)uu16[g], ug * 128);
+                dma16_asm(kv_words, lds_addr(dst + (((2 * (opaque_s(wave) & 3) + g) * 9 + ug) << 10)), rows[g], (unsigned)uu16[g], ug * 128);
             };
             // each chunk's cache row: dense -> from the page; sparse -> the
             // index entry of the chunk's token, held by the lane of that token
@@ -844,47 +852,56 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
 
         // ------------------------------------------------ epilogue
         const bool final_out = sg.n_splits == 1;
+        // V64: token-half 1 hands (m, l, O) to token-half 0 of the same rows
+        // through LDS; half 0 folds them in as it stores (o4 below), so its
+        // accumulators are read once and never rewritten.
+        float LDS_AS* xo = (float LDS_AS*)smem;                          // [2][16][4][64] float4
+        float LDS_AS* xm = (float LDS_AS*)(smem + 2 * 16 * 4 * 64 * 16);  // [2][64] m, then [2][64] l
+        float e_self = 1.f, e_part = 0.f;
         if constexpr (VAR == kV64) {
-            // token-half 1 hands (m, l, O) to token-half 0 of the same rows
-            float LDS_AS* xo = (float LDS_AS*)smem;                          // [2][16][4][64] float4
-            float LDS_AS* xm = (float LDS_AS*)(smem + 2 * 16 * 4 * 64 * 16);  // [2][64] m, then [2][64] l
             if (tw == 1) {
+                const int ln = lane_fresh();
                 #pragma unroll
                 for (int d = 0; d < NO; ++d)
                     #pragma unroll
                     for (int g = 0; g < 4; ++g)
-                        *(f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4) =
+                        *(f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + ln) * 4) =
                             f32x4{oacc[d][4 * g], oacc[d][4 * g + 1], oacc[d][4 * g + 2], oacc[d][4 * g + 3]};
-                xm[rw * 64 + lane] = m_run;
-                xm[128 + rw * 64 + lane] = l_run;
+                xm[rw * 64 + ln] = m_run;
+                xm[128 + rw * 64 + ln] = l_run;
             }
             block_sync_lds();
             if (tw == 0) {
-                const float m1 = xm[rw * 64 + lane], l1 = xm[128 + rw * 64 + lane];
+                const int ln = lane_fresh();
+                const float m1 = xm[rw * 64 + ln], l1 = xm[128 + rw * 64 + ln];
                 const float mx = fmaxf(m_run, m1);
-                const float e0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
-                const float e1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
-                #pragma unroll
-                for (int d = 0; d < NO; ++d)
-                    #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 v = *(const f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + lane) * 4);
-                        #pragma unroll
-                        for (int e = 0; e < 4; ++e) oacc[d][4 * g + e] = oacc[d][4 * g + e] * e0 + v[e] * e1;
-                    }
-                l_run = l_run * e0 + l1 * e1;
+                e_self = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                e_part = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+                l_run = l_run * e_self + l1 * e_part;
                 m_run = mx;
             }
-            block_sync_lds();  // merge buffer read before the next segment's DMA
         }
         if constexpr (R32) {
           if (VAR == kV128 || tw == 0) {
             const float l_tot = l_run + wave_shfl_xor(l_run, 32);
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-            const int rloc = 32 * rw + (lane & 31);
+            // addresses from an opaque lane id: computed here, not held
+            // across the tile loop
+            const int ln = lane_fresh();
+            const int rloc = 32 * rw + (ln & 31);
             const int h = sg.h0 + rloc;
-            const int hh = lane >> 5;
+            const int hh = ln >> 5;
+            // the 4 output values of (d, g) times a factor: this wave's
+            // (times a), plus for V64 the other token half's from LDS (times b)
+            auto o4 = [&](int d, int g, float a, float b) -> f32x4 {
+                f32x4 r = {oacc[d][4 * g] * a, oacc[d][4 * g + 1] * a, oacc[d][4 * g + 2] * a, oacc[d][4 * g + 3] * a};
+                if constexpr (VAR == kV64) {
+                    const f32x4 v = *(const f32x4 LDS_AS*)(xo + ((((rw * 16 + d) * 4 + g) * 64) + ln) * 4);
+                    r += v * b;
+                }
+                return r;
+            };
             if (final_out) {
                 if (h < p.h_q) {
                     uint16_t* op = p.o + (qrow0 + h) * F::kDv;
@@ -893,9 +910,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                         #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             const int dim = 32 * d + 8 * g + 4 * hh;
+                            const f32x4 v = o4(d, g, e_self * inv, e_part * inv);
                             i16x4 w;
                             #pragma unroll
-                            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, (__bf16)(oacc[d][4 * g + e] * inv));
+                            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, (__bf16)v[e]);
                             *(i16x4*)(op + dim) = w;
                         }
                     }
@@ -909,18 +927,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 #pragma unroll
                 for (int d = 0; d < NO; ++d)
                     #pragma unroll
-                    for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(oacc[d][v]));
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v = o4(d, g, e_self, e_part);
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+                    }
                 amax = fmaxf(amax, wave_shfl_xor(amax, 32));
+                // V64: the store pass reads the other half's values again
+                // and scales afresh instead of holding the pass above's
+                if constexpr (VAR == kV64) asm volatile("" ::: "memory");
                 const unsigned ef = partial_exp_field(amax * inv);
                 const float sc = inv * exp_field_inv_pow2(ef);  // exact: inv times a power of two
                 // (a slot holds 512 dims per row whatever the value width)
-                f16x4* wp = (f16x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + lane;
+                f16x4* wp = (f16x4*)(p.ws_o + (int64_t)sg.slot * RG * kDv) + (rw * 16 * 4) * 64 + ln;
                 #pragma unroll
                 for (int d = 0; d < NO; ++d) {
                     #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        wp[(d * 4 + g) * 64] = to_f16x4(oacc[d][4 * g] * sc, oacc[d][4 * g + 1] * sc,
-                                                        oacc[d][4 * g + 2] * sc, oacc[d][4 * g + 3] * sc);
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v = o4(d, g, e_self * sc, e_part * sc);
+                        wp[(d * 4 + g) * 64] = to_f16x4(v[0], v[1], v[2], v[3]);
+                    }
                 }
                 if (hh == 0) {
                     p.ws_lse[(int64_t)sg.slot * RG + rloc] = lse_v;
@@ -928,6 +953,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 }
             }
           }
+          if constexpr (VAR == kV64) block_sync_lds();  // merge buffer read before the next segment's DMA
         } else {
             // merge the four waves' states through LDS
             float l_w = l_run + wave_shfl_xor(l_run, 16);

@@ -205,6 +205,23 @@ __device__ __forceinline__ void dma16_asm(const u32x4& rsrc, unsigned lds, unsig
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(va), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soffset)));
 }
 
+// This lane's index in the wave (0..63), computed afresh where it is used: an
+// asm with no inputs is not hoisted out of a loop, so nothing derived from it
+// is held (or spilled) across the tile loop.
+__device__ __forceinline__ int lane_fresh() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// A wave-uniform value unchanged, but opaque to the optimiser: what is derived
+// from it inside a loop is computed there, not hoisted out of the loop and
+// held (and spilled) in scalar registers across it.
+__device__ __forceinline__ int opaque_s(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // The value unchanged, but opaque to the optimiser: lane-dependent addresses
 // computed from it inside a loop are not hoisted out of the loop (and then
 // spilled to scratch across it).
