@@ -82,10 +82,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // consecutive logical parts (same sequence) share an XCD and its L2.
     int part = blockIdx.x;
     if ((gridDim.x & 7) == 0) part = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int32_t* tm = p.tile_meta + (int64_t)part * 8;
-    if (uniform(tm[5])) return;
-    const int qb = uniform(tm[0]), tb = uniform(tm[1]), qe = uniform(tm[2]), te = uniform(tm[3]);
-    const int fs = uniform(tm[4]);
+    // the part's schedule row: one scalar load of all its fields, then the
+    // empty test (testing first would make the other fields a second round trip)
+    typedef const int32_t __attribute__((address_space(4))) cint32_t;
+    const cint32_t* tm = (const cint32_t*)p.tile_meta + (int64_t)part * 8;
+    const int qb = tm[0], tb = tm[1], qe = tm[2], te = tm[3], fs = tm[4], empty = tm[5];
+    if (empty) return;
 
     const __amdgpu_buffer_rsrc_t kv_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)p.row_bytes, p.num_rows, 0x00020000);
@@ -108,11 +110,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // words past the segment's last tile are never used.
         auto load_index = [&](int k, int kmax) -> unsigned {
             unsigned r = kOOB;
-            if (k <= kmax) {
-                if (SPARSE) {
-                    const int pos = k * kBlock + lane_fresh();
-                    if (pos < p.topk) r = (unsigned)idx_row[pos];
-                } else if constexpr (kScalarIdx) {
+            if constexpr (SPARSE) {
+                // branch-free and unchecked: the load is always issued, at a
+                // position clamped into the row (topk >= 1), and its value is
+                // not used here, so no wait for it lands here; tile_src drops
+                // the entries past topk, and words past the segment are unused
+                r = (unsigned)idx_row[min(k * kBlock + lane_fresh(), p.topk - 1)];
+            } else if (k <= kmax) {
+                if constexpr (kScalarIdx) {
                     // read-only for the whole kernel: a scalar load (lgkmcnt),
                     // outside the vmcnt count that tracks the tile loads
                     typedef const int32_t __attribute__((address_space(4))) cint32;
@@ -156,7 +161,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         }
         // read-only for the whole kernel: scalar loads (lgkmcnt), so that the
         // wait for them does not also wait for the VMEM loads above
-        typedef const int32_t __attribute__((address_space(4))) cint32_t;
         const int len_raw = SPARSE ? 0 : ((cint32_t*)p.seqlens)[sg.b];
         const int so_raw = ((cint32_t*)p.split_offsets)[qq], so_end_raw = ((cint32_t*)p.split_offsets)[qq + 1];
 
@@ -178,6 +182,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const int dim0 = R32 ? 16 * kk : 32 * kk;
                 qreg[kk] = __builtin_bit_cast(bf16x8, *(const i16x8*)(qbase + qoff + dim0));
             }
+            // issue the q loads here, before the waits for the length and the
+            // index words below (left to itself the compiler sinks them past
+            // the test for an empty segment, behind that wait)
+            asm volatile("" ::: "memory");
         }
 
         int T_q;
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     const int t = tg * 8 + (ln >> 3);
                     const int uu = (ln & 7) ^ ((t >> 1) & 7);
                     unsigned row;
-                    if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
+                    if (SPARSE) row = (unsigned)wave_shfl((int)srow, t);
                     else row = dense_row(page0, n_valid, t);
                     if constexpr (UNROLL) {
                         #pragma unroll
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 int u = kk0 - t * F::kRawUnits;
                 auto chunk = [&](int c) {
                     unsigned row;
-                    if (SPARSE) row = (unsigned)__shfl((int)srow, t, 64);
+                    if (SPARSE) row = (unsigned)wave_shfl((int)srow, t);
                     else row = dense_row(page0, n_valid, t);
                     tile_load(dst + (c << 10), row, (unsigned)(u << 4), 0);
                     u += kStepU;
@@ -769,7 +777,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             auto tile_rows = [&](const TileSrc& tsrc, unsigned (&rows)[2]) {
                 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
-                    if constexpr (SPARSE) rows[g] = (unsigned)__shfl((int)tsrc.srow, trow[g], 64);
+                    if constexpr (SPARSE) rows[g] = (unsigned)wave_shfl((int)tsrc.srow, trow[g]);
                     else rows[g] = dense_row(tsrc.page0, tsrc.n_valid, trow[g]);
                 }
             };

@@ -230,7 +230,13 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-__device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+// The value of lane (this lane ^ m), 0 < m < 64, as one ds_bpermute (the
+// lane id computed afresh: nothing is held across loops for it).
+__device__ __forceinline__ float wave_shfl_xor(float v, int m) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_fresh() ^ m) << 2, __float_as_int(v)));
+}
+// The value of lane src (0..63), as one ds_bpermute.
+__device__ __forceinline__ int wave_shfl(int v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
 
 // bf16x8 from eight floats (round to nearest even).
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6, float a7) {
