@@ -22,6 +22,9 @@ from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_mi355x.so")
+# the race-check build: the split kernel waits for each tile's loads right
+# after issuing them (same entry points; used only by the LDS race check)
+DRAIN_LIB_PATH = os.path.join(HERE, "libmla_mi355x_drain.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID = -1
@@ -88,11 +91,26 @@ _lib = None
 def lib() -> ctypes.CDLL:
     """Load libmla_mi355x.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m mla_latent_kv_10_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+_drain_lib = None
+
+
+def drain_lib() -> ctypes.CDLL:
+    """Load the race-check build libmla_mi355x_drain.so (same entry points)."""
+    global _drain_lib
+    if _drain_lib is None:
+        _drain_lib = _load(DRAIN_LIB_PATH)
+    return _drain_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with `python -m mla_latent_kv_10_amd.build`")
+    L = ctypes.CDLL(path)
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
     L.mla_default_num_parts.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -112,7 +130,6 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_void_p]
     for name in EXPORTS:
         getattr(L, name).restype = ctypes.c_char_p if name == "mla_last_error" else ctypes.c_int
-    _lib = L
     return L
 
 

@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# The same library with the split kernel built to wait for every tile's loads
+# right after issuing them (MLA_DRAIN_PIPELINE): the LDS race check compares
+# its outputs with the pipelined library's, bit for bit.
+DRAIN_LIB_PATH = os.path.join(HERE, "libmla_mi355x_drain.so")
 SOURCES = ["mla_abi.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_combine.hip", "mla_quantize.hip", "mla_absorb.hip"]
 
 ARCH = "gfx950"
@@ -56,24 +60,30 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     hipcc = _hipcc()
     tmp = tempfile.mkdtemp(prefix="mla_build_")
     try:
-        def compile_one(src):
-            obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        def compile_one(job):
+            src, tag, defs = job
+            obj = os.path.join(tmp, os.path.basename(src) + tag + ".o")
+            cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *defs, "-x", "hip", "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
             if verbose:
-                print(f"compiled {src}", flush=True)
+                print(f"compiled {src}{tag}", flush=True)
             return obj
 
+        jobs_list = [(src, "", []) for src in SOURCES] + [("mla_decode.hip", ".drain", ["-DMLA_DRAIN_PIPELINE"])]
         with ThreadPoolExecutor(max_workers=jobs) as ex:
-            objs = list(ex.map(compile_one, SOURCES))
-        out_tmp = LIB_PATH + ".tmp"
-        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB_PATH)
+            objs = list(ex.map(compile_one, jobs_list))
+        main_objs = objs[:len(SOURCES)]
+        drain_objs = [objs[-1] if src == "mla_decode.hip" else o for src, o in zip(SOURCES, main_objs)]
+        for path, parts in ((LIB_PATH, main_objs), (DRAIN_LIB_PATH, drain_objs)):
+            out_tmp = path + ".tmp"
+            cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", out_tmp]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+            os.replace(out_tmp, path)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     if verbose:

@@ -43,6 +43,16 @@ namespace {
 
 using namespace dev;
 
+// A race-check build (MLA_DRAIN_PIPELINE defined) waits for every tile's loads
+// right after issuing them, so each lands at the earliest point the schedule
+// allows; its outputs must equal the pipelined build's bit for bit. A load
+// issued into LDS that a wave may still read would show up as a difference.
+#ifdef MLA_DRAIN_PIPELINE
+constexpr bool kDrainPipeline = true;
+#else
+constexpr bool kDrainPipeline = false;
+#endif
+
 // ---------------------------------------------------------------- kernel
 
 template <int FMT, bool SPARSE, int VAR>
@@ -702,11 +712,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             uint64_t mask_a = ts.mask, mask_b = 0;
             #pragma unroll
             for (int j = 0; j < F::kRawSlots; ++j) raw_chunk(j, raw0, ts);
+            if constexpr (kDrainPipeline) wait_vm(0);
             if (t0 + 1 <= t1) {
                 ts = tile_src(t0 + 1, word_of(t0 + 1, idx_b));
                 mask_b = ts.mask;
                 #pragma unroll
                 for (int j = 0; j < F::kRawSlots; ++j) raw_chunk(j, raw1, ts);
+                if constexpr (kDrainPipeline) wait_vm(0);
             }
             // q was loaded before these tiles: have it in registers here. (The
             // compiler does not see the tile loads, so its wait for q also
@@ -739,6 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
                     if (j < F::kRawSlots) {
                         chunk_issue(j, cur, ca);
+                        if (kDrainPipeline && j == F::kRawSlots - 1) wait_vm(0);
                         if (j + 1 < F::kRawSlots) ca = chunk_addr(j + 1, tn);
                     }
                 });
@@ -787,6 +800,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             tile_rows(ts, rows0);
             #pragma unroll
             for (int j = 0; j < 18; ++j) qk_chunk(j, buf0, rows0);
+            if constexpr (kDrainPipeline) wait_vm(0);
             // q was loaded before the tile: have it in registers here.
             #pragma unroll
             for (int kk = 0; kk < NQ; ++kk) asm volatile("" ::"v"(qreg[kk]));
@@ -805,7 +819,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const TileSrc tn = (k + 1 <= t1) ? tile_src(k + 1, idx_n) : none;
                 unsigned rows[2];
                 tile_rows(tn, rows);
-                compute_tile(cur, mask_a, std::true_type{}, [&](int j) { qk_chunk(j, nxt, rows); });
+                compute_tile(cur, mask_a, std::true_type{}, [&](int j) {
+                    qk_chunk(j, nxt, rows);
+                    if (kDrainPipeline && j == 17) wait_vm(0);
+                });
                 mask_a = tn.mask;
                 idx_n = idx_f;
             }
@@ -821,6 +838,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             constexpr std::false_type kLooped{};
             uint64_t mask_a = issue_tile(kUnrolled, t0, stage0, idx_a), mask_b = 0;
             if (t0 + 1 <= t1) mask_b = issue_tile(kUnrolled, t0 + 1, stage1, idx_b);
+            if constexpr (kDrainPipeline) wait_vm(0);
             // q was loaded before these tiles: have it in registers here, with the
             // tiles still in flight, so no wait for it lands inside the tile loop.
             #pragma unroll
@@ -846,11 +864,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     dequant(cur, ctile);
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
+                    if constexpr (kDrainPipeline) wait_vm(0);
                     compute_tile(ctile, mask_a, std::false_type{}, [](int) {});
                 } else {
                     compute_tile(cur, mask_a, std::false_type{}, [](int) {});
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
+                    if constexpr (kDrainPipeline) wait_vm(0);
                 }
                 idx_a = idx_b; idx_b = idx_c; idx_c = idx_d;
                 mask_a = mask_b; mask_b = mask_c;

@@ -28,9 +28,13 @@ VMEM_LOAD = re.compile(r"^(global_load|buffer_load|flat_load)")
 
 @pytest.fixture(scope="module")
 def functions():
-    lib = B.LIB_PATH
-    if not os.path.exists(lib):
+    if not os.path.exists(B.LIB_PATH):
         pytest.skip("library not built")
+    return _decode_functions(B.LIB_PATH)
+
+
+def _decode_functions(lib):
+    """{(format, sparse, variant): [(address, instruction, branch target)]} of the decode kernels."""
     for t in TOOLS:
         if not os.path.exists(os.path.join(LLVM, t)):
             pytest.skip(f"{t} not found")
@@ -111,3 +115,16 @@ def test_sparse_ring_wait_counts_only_later_loads(functions, fmt):
 
 def test_library_is_the_one_the_binding_loads():
     assert os.path.samefile(m.lib()._name, B.LIB_PATH)
+
+
+def test_race_check_build_drains_every_pipeline():
+    """The race-check library waits vmcnt(0) more often in every decode kernel."""
+    if not os.path.exists(B.DRAIN_LIB_PATH):
+        pytest.skip("race-check library not built")
+    main = _decode_functions(B.LIB_PATH)
+    drain = _decode_functions(B.DRAIN_LIB_PATH)
+    assert sorted(main) == sorted(drain)
+    for key in main:
+        n_main = sum(1 for _, ins, _ in main[key] if ins == "s_waitcnt vmcnt(0)")
+        n_drain = sum(1 for _, ins, _ in drain[key] if ins == "s_waitcnt vmcnt(0)")
+        assert n_drain > n_main, (key, n_main, n_drain)
