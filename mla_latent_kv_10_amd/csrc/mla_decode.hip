@@ -930,7 +930,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 }
                 return r;
             };
-            if (final_out) {
+            if (final_out && VAR == kV128) {
+                // Rows leave through LDS (free once the tile loop is done): a
+                // lane holds 4 dims of one row per accumulator group, so direct
+                // stores would write 32 separate 16-byte pieces per instruction.
+                // Staged, each store writes one row's half contiguously. Per
+                // wave 32 rows x half the dims, rows padded by 8 dims.
+                constexpr int kHalfD = 32 * (NO / 2);            // dims per half (256, or 224)
+                constexpr int kStg = kHalfD + 8;                  // staged row stride (dims)
+                uint16_t LDS_AS* stg = (uint16_t LDS_AS*)(kFp8Pipe ? (char LDS_AS*)lds_tile : smem) + wave * 32 * kStg;
+                const int rl = ln & 31;
+                #pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    #pragma unroll
+                    for (int dd = 0; dd < NO / 2; ++dd) {
+                        const int d = half * (NO / 2) + dd;
+                        #pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f32x4 v = o4(d, g, e_self * inv, e_part * inv);
+                            i16x4 w;
+                            #pragma unroll
+                            for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(short, (__bf16)v[e]);
+                            *(i16x4 LDS_AS*)(stg + rl * kStg + 32 * dd + 8 * g + 4 * hh) = w;
+                        }
+                    }
+                    // the wave reads back what it wrote (LDS ops of one wave stay in order)
+                    #pragma unroll 4
+                    for (int r = 0; r < 32; ++r) {
+                        const int hr = sg.h0 + 32 * rw + r;
+                        if (hr < p.h_q && 4 * ln < kHalfD) {
+                            const i16x4 w = *(const i16x4 LDS_AS*)(stg + r * kStg + 4 * ln);
+                            *(i16x4*)(p.o + (qrow0 + hr) * F::kDv + half * kHalfD + 4 * ln) = w;
+                        }
+                    }
+                }
+                if (hh == 0 && h < p.h_q) p.lse[qrow0 + h] = lse_v;
+                block_sync_lds();  // every wave has read its staged rows before the next segment's loads
+            } else if (final_out) {
                 if (h < p.h_q) {
                     uint16_t* op = p.o + (qrow0 + h) * F::kDv;
                     #pragma unroll
