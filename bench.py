@@ -222,8 +222,8 @@ def quantize_cpu_baseline(src, seconds: float):
             "sample": f"{done} rows of the same workload in chunks of {chunk}, NumPy float32, {dt:.1f} s"}
 
 
-def bench_quantize(args):
-    """Time mla_quantize_fp8_append writing a whole FP8 cache."""
+def bench_quantize(args, emit: bool = True):
+    """Time mla_quantize_fp8_append writing a whole FP8 cache (print the JSON line, or return it)."""
     import torch
 
     import mla_latent_kv_10_amd as mla
@@ -269,6 +269,8 @@ def bench_quantize(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = quantize_cpu_baseline(src_cpu, args.cpu_seconds)
+    if not emit:
+        return out
     print(json.dumps(out), flush=True)
 
 
@@ -286,8 +288,9 @@ def absorb_counts(T: int, H: int):
     return absorb_bytes, unabsorb_bytes, flops
 
 
-def bench_absorb(args):
-    """Time mla_absorb_q and mla_unabsorb_o at the FP8 causal workload's token count (64 x 2 tokens, 128 heads)."""
+def bench_absorb(args, emit: bool = True):
+    """Time mla_absorb_q and mla_unabsorb_o at the FP8 causal workload's token count (64 x 2 tokens, 128
+    heads); print the JSON line, or return it."""
     import torch
 
     import mla_latent_kv_10_amd as mla
@@ -364,6 +367,8 @@ def bench_absorb(args):
         out["cpu_baseline"] = {"value": round(done * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{done} tokens of the same inputs in groups of 8, float64 NumPy, {dt:.1f} s"}
+    if not emit:
+        return out
     print(json.dumps(out), flush=True)
 
 
@@ -670,6 +675,14 @@ def main():
     if sweep is not None:
         out["sweep"] = sweep
         out["configs"] = extras
+        # the rows beside the decode: the FP8 cache writer and the absorption
+        # products, each with its own roofline (no CPU leg here)
+        side = argparse.Namespace(steps=200, warmup=5, no_cpu_baseline=True, cpu_seconds=0.0)
+        keep = ("value", "unit", "ms_per_step", "config", "kernel_source_hash", "roofline")
+        out["ops"] = {"quantize": {k: v for k, v in bench_quantize(side, emit=False).items() if k in keep},
+                      "absorb": {k: v for k, v in bench_absorb(side, emit=False).items()
+                                 if k in keep + ("absorb_q_ms", "unabsorb_o_ms", "tflops")}}
+        progress(f"ops: quantize {out['ops']['quantize']['value']} GB/s, absorb {out['ops']['absorb']['value']} GB/s")
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_seconds)
         cb["cpu_model"] = cpu_model()
