@@ -377,7 +377,7 @@ HEADLINE_L = 65536
 # (key, config number) of the workloads reported beside the sweep
 EXTRA_CONFIGS = (("dense_bf16_h128", 2), ("fp8_causal_h128", 4), ("sparse_fp8_h128", 5),
                  ("sparse_prefill_bf16", 6), ("dense_bf16_h64", 7), ("fp8_528_causal_h128", 8),
-                 ("sparse_fp8_528_h128", 9))
+                 ("sparse_fp8_528_h128", 9), ("lowhead_two_position_bf16", 10))
 
 
 def cpu_model() -> str:
@@ -572,8 +572,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=0,
-                    help="one workload only (1..9; 3 takes --seqlen); default: the length sweep of workload 3 "
-                         "with workloads 2 and 4..9 beside it")
+                    help="one workload only (1..10; 3 takes --seqlen); default: the length sweep of workload 3 "
+                         "with workloads 2 and 4..10 beside it")
     ap.add_argument("--seqlen", type=int, default=HEADLINE_L, help="sequence length for workload 3")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -64,11 +64,17 @@ extern "C" {
 /*
  * Split policy (the library's own rule; the pages give the metadata's role,
  * [Walkthrough] §七 "split-KV", but no format):
- *   Query rows are grouped into "row groups" of RG heads of one query
- *   position: RG = 16 when h_q <= 16, RG = 64 when 16 < h_q <= 64, else
- *   RG = 128. A row-group sequence q = b * n_rg + i * n_hb + hb, with
- *   n_hb = ceil(h_q / RG) head blocks and
- *   n_rg = s_q * n_hb, covers T_q = ceil(L_b / 64) tiles of 64 tokens (dense)
+ *   The query rows of sequence b are its rows of q in order, (position i,
+ *   head h) -> i * h_q + h. A dense call (topk == 0) puts all R = s_q * h_q
+ *   of them in one row space: they attend the same cache, so one pass over
+ *   it serves every position ([Walkthrough] §七 "先算清楚瓶颈": a decode
+ *   request's h_q * s_q query rows share the KV). A sparse call has s_q row spaces of R = h_q
+ *   rows, one per position (each position has its own indices). Rows are
+ *   grouped into "row groups" of RG consecutive rows of a row space: RG = 16
+ *   when R <= 16, RG = 64 when 16 < R <= 64, else RG = 128. A row-group
+ *   sequence q = b * n_rg + i * n_hb + hb, with n_hb = ceil(R / RG) and
+ *   n_rg = n_pos * n_hb (n_pos = 1 dense, s_q sparse; i = the row space),
+ *   covers T_q = ceil(L_b / 64) tiles of 64 tokens (dense)
  *   or ceil(topk / 64) tiles (sparse). Units are laid end to end, each
  *   non-empty one first taking FIXED_COST positions, then one per tile; with
  *   total = sum(FIXED_COST + T_q) and W = max(ceil(total / num_parts),
@@ -92,14 +98,17 @@ int mla_default_num_parts(int device, int* num_parts);
 /*
  * Element counts of the two metadata buffers for a call shape:
  * tile_meta holds num_parts * 8 int32, split_offsets holds Q + 1 int32 where
- * Q = batch * n_rg. Pure host arithmetic.
+ * Q = batch * n_rg, the larger of the dense and the sparse n_rg (the sizes do
+ * not depend on topk, so they cover either kind of call; a shape whose sparse
+ * Q exceeds MLA_MAX_UNITS gets the dense sizes). Pure host arithmetic.
  */
 int mla_metadata_size(int batch, int s_q, int h_q, int num_parts,
                       int64_t* tile_meta_elems, int64_t* split_offsets_elems);
 
 /*
- * Bytes of split workspace mla_decode_with_kvcache needs. Layout, with
- * S = Q + num_parts slots: partial outputs, S slots of RG x 512 fp16; then, at
+ * Bytes of split workspace mla_decode_with_kvcache needs: enough for a dense
+ * or a sparse call of this shape (the larger). Layout, with
+ * S = Q + num_parts slots (Q and RG of the call's kind): partial outputs, S slots of RG x 512 fp16; then, at
  * the next 256-byte boundary, partial lse fp32 [S][RG]; then partial scales
  * fp32 [S][RG]. A partial row o_k (already divided by its own softmax sum) is
  * stored as fp16(o_k / c), c = its scale, a power of two chosen so that the

@@ -1,6 +1,7 @@
 // C ABI of the library (declared in include/mla.h): argument validation on
 // the host, buffer sizing, and kernel launches. Every check runs before any
 // HIP call so that an invalid call enqueues nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -31,26 +32,46 @@ int ok() {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-int check_shape(int batch, int s_q, int h_q, int num_parts) {
+bool fits(int batch, int s_q, int h_q, bool sparse) {
+    return (int64_t)batch * mla::layout_for(h_q, s_q, sparse).n_rg <= mla::kMaxUnits;
+}
+
+// Shape checks. mode: 0 dense, 1 sparse, -1 the size queries, which do not
+// know the kind of call: they cover every kind the shape allows (a sparse
+// shape has at least as many row groups as the dense one, so dense is the
+// one that can fit alone).
+int check_shape(int batch, int s_q, int h_q, int num_parts, int mode) {
     if (batch < 1) return fail(MLA_ERR_INVALID, "batch must be >= 1 (got %d)", batch);
     if (s_q < 1) return fail(MLA_ERR_INVALID, "s_q must be >= 1 (got %d)", s_q);
     if (h_q < 1) return fail(MLA_ERR_INVALID, "h_q must be >= 1 (got %d)", h_q);
     if (num_parts < 1 || num_parts > 65535)
         return fail(MLA_ERR_INVALID, "num_parts must be in [1, 65535] (got %d)", num_parts);
-    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
-    const int64_t Q = (int64_t)batch * l.n_rg;
-    if (Q > mla::kMaxUnits)
-        return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * ceil(h_q / %d) = %lld exceeds %d row-group sequences",
-                    l.rg, (long long)Q, mla::kMaxUnits);
+    const bool sparse = mode == 1;
+    if (!fits(batch, s_q, h_q, sparse)) {
+        const mla::Layout l = mla::layout_for(h_q, s_q, sparse);
+        return fail(MLA_ERR_UNSUPPORTED, "%s: batch * %d row groups of %d rows = %lld exceeds %d row-group sequences",
+                    sparse ? "sparse" : "dense", l.n_rg, l.rg, (long long)batch * l.n_rg, mla::kMaxUnits);
+    }
     return MLA_OK;
 }
 
-size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
-    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
+size_t workspace_bytes_for(int batch, int num_parts, const mla::Layout& l) {
     const size_t slots = (size_t)batch * l.n_rg + (size_t)num_parts;
     const size_t o_bytes = slots * l.rg * mla::kDv * sizeof(uint16_t);
     const size_t lse_bytes = slots * l.rg * sizeof(float);
     return ((o_bytes + 255) & ~(size_t)255) + 2 * lse_bytes;
+}
+
+// Workspace bytes of a call (mode 0 dense, 1 sparse) or, for mode -1, enough
+// for every kind of call the shape allows.
+size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts, int mode) {
+    size_t need = 0;
+    for (int m = 0; m < 2; ++m) {
+        if (mode >= 0 ? m != mode : !fits(batch, s_q, h_q, m == 1)) continue;
+        const size_t b = workspace_bytes_for(batch, num_parts, mla::layout_for(h_q, s_q, m == 1));
+        need = b > need ? b : need;
+    }
+    return need;
 }
 
 // Validates a decode call; fills the kernel parameters.
@@ -59,7 +80,8 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (a->struct_size != (int32_t)sizeof(mla_decode_args))
         return fail(MLA_ERR_INVALID, "struct_size %d != sizeof(mla_decode_args) %d", a->struct_size,
                     (int)sizeof(mla_decode_args));
-    int st = check_shape(a->batch, a->s_q, a->h_q, a->num_parts);
+    const bool sparse = a->indices != nullptr;
+    int st = check_shape(a->batch, a->s_q, a->h_q, a->num_parts, sparse ? 1 : 0);
     if (st) return st;
     if (!a->q || !a->kv || !a->o || !a->lse) return fail(MLA_ERR_INVALID, "q, kv, o and lse must be non-NULL");
     if (!aligned(a->q, 16) || !aligned(a->o, 16) || !aligned(a->kv, 16) || !aligned(a->lse, 4))
@@ -80,7 +102,6 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (a->num_blocks * (int64_t)mla::kBlock * a->row_bytes > ((int64_t)1 << 32))
         return fail(MLA_ERR_UNSUPPORTED, "the cache (num_blocks * 64 * row_bytes = %lld bytes) must be at most 4 GiB",
                     (long long)(a->num_blocks * (int64_t)mla::kBlock * a->row_bytes));
-    const bool sparse = a->indices != nullptr;
     if (sparse) {
         if (a->topk < 1) return fail(MLA_ERR_INVALID, "topk must be >= 1 with indices");
         if (a->causal) return fail(MLA_ERR_INVALID, "causal masking is not defined with sparse indices");
@@ -100,11 +121,11 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     if (!a->tile_meta || !a->split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
     if (!a->workspace) return fail(MLA_ERR_INVALID, "workspace is required");
     if (!aligned(a->workspace, 256)) return fail(MLA_ERR_INVALID, "workspace must be 256-byte aligned");
-    const size_t need = workspace_bytes(a->batch, a->s_q, a->h_q, a->num_parts);
+    const size_t need = workspace_bytes(a->batch, a->s_q, a->h_q, a->num_parts, sparse ? 1 : 0);
     if (a->workspace_bytes < need)
         return fail(MLA_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", a->workspace_bytes, need);
 
-    const mla::Layout l = mla::layout_for(a->h_q, a->s_q, a->batch, a->num_parts);
+    const mla::Layout l = mla::layout_for(a->h_q, a->s_q, sparse);
     const size_t slots = (size_t)a->batch * l.n_rg + (size_t)a->num_parts;
     const size_t o_bytes = ((slots * l.rg * mla::kDv * sizeof(uint16_t)) + 255) & ~(size_t)255;
     p->q = static_cast<const uint16_t*>(a->q);
@@ -125,6 +146,8 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     p->n_hb = l.n_hb;
     p->n_rg = l.n_rg;
     p->rg = l.rg;
+    p->rows_b = l.rows_b;
+    p->n_pos = l.n_pos;
     p->mbps = sparse ? 0 : a->max_blocks_per_seq;
     p->topk = sparse ? a->topk : 0;
     p->causal = a->causal ? 1 : 0;
@@ -153,32 +176,33 @@ int mla_default_num_parts(int device, int* num_parts) {
 int mla_metadata_size(int batch, int s_q, int h_q, int num_parts, int64_t* tile_meta_elems,
                       int64_t* split_offsets_elems) {
     if (!tile_meta_elems || !split_offsets_elems) return fail(MLA_ERR_INVALID, "output pointers are NULL");
-    int st = check_shape(batch, s_q, h_q, num_parts);
+    int st = check_shape(batch, s_q, h_q, num_parts, -1);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
+    int n_rg = mla::layout_for(h_q, s_q, false).n_rg;
+    if (fits(batch, s_q, h_q, true)) n_rg = std::max(n_rg, mla::layout_for(h_q, s_q, true).n_rg);
     *tile_meta_elems = (int64_t)num_parts * 8;
-    *split_offsets_elems = (int64_t)batch * l.n_rg + 1;
+    *split_offsets_elems = (int64_t)batch * n_rg + 1;
     return ok();
 }
 
 int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes) {
     if (!bytes) return fail(MLA_ERR_INVALID, "bytes is NULL");
-    int st = check_shape(batch, s_q, h_q, num_parts);
+    int st = check_shape(batch, s_q, h_q, num_parts, -1);
     if (st) return st;
-    *bytes = workspace_bytes(batch, s_q, h_q, num_parts);
+    *bytes = workspace_bytes(batch, s_q, h_q, num_parts, -1);
     return ok();
 }
 
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int topk, int num_parts,
                      int32_t* tile_meta, int32_t* split_offsets, void* stream) {
-    int st = check_shape(batch, s_q, h_q, num_parts);
+    int st = check_shape(batch, s_q, h_q, num_parts, topk > 0 ? 1 : 0);
     if (st) return st;
     if (topk < 0) return fail(MLA_ERR_INVALID, "topk must be >= 0 (got %d)", topk);
     if (topk > mla::kMaxSeqTokens) return fail(MLA_ERR_UNSUPPORTED, "topk must be <= 2^23 (got %d)", topk);
     if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
     if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
     if (!aligned(tile_meta, 16)) return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned");
-    const mla::Layout l = mla::layout_for(h_q, s_q, batch, num_parts);
+    const mla::Layout l = mla::layout_for(h_q, s_q, topk > 0);
     mla::MetaParams p;
     p.seqlens = cache_seqlens;
     p.tile_meta = tile_meta;
@@ -201,7 +225,7 @@ int mla_decode_with_kvcache(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = prepare(args, &p);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
+    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->indices != nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = mla::launch_decode(p, l.variant, args->kv_format, args->indices != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -214,7 +238,7 @@ int mla_decode_splits(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = prepare(args, &p);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->batch, args->num_parts);
+    const mla::Layout l = mla::layout_for(args->h_q, args->s_q, args->indices != nullptr);
     hipError_t e = mla::launch_decode(p, l.variant, args->kv_format, args->indices != nullptr,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -273,9 +297,9 @@ int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream) {
     if (args->struct_size != (int32_t)sizeof(mla_decode_args))
         return fail(MLA_ERR_INVALID, "struct_size %d != sizeof(mla_decode_args) %d", args->struct_size,
                     (int)sizeof(mla_decode_args));
-    int st = check_shape(args->batch, args->s_q, args->h_q, args->num_parts);
+    int st = check_shape(args->batch, args->s_q, args->h_q, args->num_parts, args->indices != nullptr ? 1 : 0);
     if (st) return st;
-    const size_t need = workspace_bytes(args->batch, args->s_q, args->h_q, args->num_parts);
+    const size_t need = workspace_bytes(args->batch, args->s_q, args->h_q, args->num_parts, args->indices != nullptr ? 1 : 0);
     if (need > (size_t)MLA_STATIC_SCRATCH_BYTES)
         return fail(MLA_ERR_UNSUPPORTED,
                     "this call needs %zu bytes of split workspace; the static scratch holds %zu "
@@ -295,7 +319,7 @@ int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream) {
     a.workspace = ptr;
     st = prepare(&a, &p);
     if (st) return st;
-    const mla::Layout l = mla::layout_for(a.h_q, a.s_q, a.batch, a.num_parts);
+    const mla::Layout l = mla::layout_for(a.h_q, a.s_q, a.indices != nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = mla::launch_decode(p, l.variant, a.kv_format, a.indices != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

@@ -88,12 +88,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     const int i = rgi / p.n_hb;
     int row, f4[M::kVec], dim[M::kVec];
     M::map(blk, threadIdx.x, row, f4, dim);
-    const int h = (rgi - i * p.n_hb) * RG + row;
-    if (h >= p.h_q) return;
+    const int h = (rgi - i * p.n_hb) * RG + row;  // row of the row space (see Layout)
+    if (h >= p.rows_b) return;
     const int s0 = split_offsets[q];
     const int n = split_offsets[q + 1] - s0;
     if (n == 1) return;  // the split kernel wrote the final row
-    const int64_t orow = ((int64_t)b * p.s_q + i) * p.h_q + h;
+    const int64_t orow = ((int64_t)b * p.n_pos + i) * p.rows_b + h;
     uint16_t* op = p.o + orow * DV;
     const bool lse_writer = dim[0] == 0;  // exactly one thread per row holds dim 0
     constexpr int kSlotBytes = RG * kDv * 2;  // fp16 partial rows of one slot

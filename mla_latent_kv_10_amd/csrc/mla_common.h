@@ -32,31 +32,40 @@ enum Variant { kV128 = 0, kV16 = 1, kV64 = 2 };
 enum Format { kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp8Mx = 2 };
 
 // Row-group policy; it is part of the ABI contract (see include/mla.h).
+//
+// The rows of a batch entry are its query rows in q's order, (position i,
+// head h) -> row i * h_q + h. A dense call packs all s_q positions of a
+// sequence into one row space of R = s_q * h_q rows: they attend the same
+// cache, so one pass over it serves them all (row i sees the first
+// L - s_q + 1 + i tokens when causal). A sparse call keeps one row space of
+// h_q rows per position: each position has its own index list.
+// R <= 16: 16-row groups (four waves splitting each tile's tokens);
+// 16 < R <= 64: 64-row groups (two row waves x two token waves);
+// R > 64: 128-row groups (four row waves, every token).
 struct Layout {
-    int rg;           // heads per row group
-    int n_hb;         // head blocks
-    int n_rg;         // row groups per batch entry (s_q * n_hb)
+    int rg;           // rows per row group
+    int rows_b;       // rows of one row space: s_q * h_q (dense), h_q (sparse)
+    int n_pos;        // row spaces per batch entry: 1 (dense), s_q (sparse)
+    int n_hb;         // row groups per row space
+    int n_rg;         // row groups per batch entry (n_pos * n_hb)
     int fixed_cost;   // schedule positions charged per row-group sequence
     int min_payload;  // minimum schedule positions per part
     int variant;
 };
 
-// h_q <= 16: one 16-head group per query position, four waves splitting each
-// tile's tokens. 16 < h_q <= 64: 64-head groups (two row waves x two token
-// waves). h_q > 64: 128-head groups (four row waves, every token).
-inline Layout layout_for(int h_q, int s_q, int batch, int num_parts) {
-    (void)batch;
-    (void)num_parts;
+inline Layout layout_for(int h_q, int s_q, bool sparse) {
     Layout l;
-    if (h_q <= 16) {
+    l.rows_b = sparse ? h_q : s_q * h_q;
+    l.n_pos = sparse ? s_q : 1;
+    if (l.rows_b <= 16) {
         l.rg = 16; l.fixed_cost = 0; l.min_payload = 1; l.variant = kV16;
-    } else if (h_q <= 64) {
+    } else if (l.rows_b <= 64) {
         l.rg = 64; l.fixed_cost = 2; l.min_payload = 2; l.variant = kV64;
     } else {
         l.rg = 128; l.fixed_cost = 2; l.min_payload = 3; l.variant = kV128;
     }
-    l.n_hb = (h_q + l.rg - 1) / l.rg;
-    l.n_rg = s_q * l.n_hb;
+    l.n_hb = (l.rows_b + l.rg - 1) / l.rg;
+    l.n_rg = l.n_pos * l.n_hb;
     return l;
 }
 
@@ -81,6 +90,7 @@ struct DecodeParams {
     uint16_t* o;                // bf16 bits [B, s_q, h_q, 512]
     float* lse;                 // [B, s_q, h_q]
     int batch, s_q, h_q, n_hb, n_rg, rg, mbps, topk, causal, num_rows, num_parts, row_bytes;
+    int rows_b, n_pos;          // the row spaces (see Layout)
     float scale_log2;           // softmax_scale * log2(e)
 };
 

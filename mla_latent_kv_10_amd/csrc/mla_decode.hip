@@ -55,8 +55,13 @@ constexpr bool kDrainPipeline = false;
 
 // ---------------------------------------------------------------- kernel
 
-template <int FMT, bool SPARSE, int VAR>
+// MIXED (dense, causal only): some row group holds rows of more than one query
+// position, so tokens between the first and the last row's causal limit are
+// masked per row. A separate instantiation keeps that masking, and the scalar
+// registers it holds across the tile loop, out of every other kernel.
+template <int FMT, bool SPARSE, int VAR, bool MIXED>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
+    static_assert(!(SPARSE && MIXED), "a sparse row group holds one position");
     using F = Fmt<FMT>;
     using S = Smem<FMT>;
     constexpr bool FP8 = F::kRaw;  // raw FP8 rows, dequantised in LDS
@@ -82,6 +87,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) char lds_raw1[kFp8Pipe ? F::kRawTile + 1024 : 1024];
     // sparse index words of four tiles (tile x in slot x & 3), 64 per tile
     __shared__ __attribute__((aligned(256))) int32_t lds_ring[kFp8Pipe && SPARSE ? 4 * 64 : 1];
+    // per wave, a dense unit's per-row cut data (first row's limit, its
+    // position, the unit's first row): kept here rather than in registers
+    // across the tile loop; each wave reads only what it wrote
+    __shared__ __attribute__((aligned(16))) int32_t lds_cut[4][4];
     char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
     const int tid = threadIdx.x;
@@ -111,7 +120,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         sg.i = rgi / p.n_hb;
         sg.h0 = (rgi - sg.i * p.n_hb) * RG;
         const int t0 = (qq == qb) ? tb : 0;
-        const int64_t qrow0 = ((int64_t)sg.b * p.s_q + sg.i) * p.h_q;  // row index of head 0
+        // global index of the row space's row 0: rows h < rows_b of this unit
+        // are q rows qrow0 + h (dense: all positions of sequence b; sparse:
+        // position i of sequence b)
+        const int64_t qrow0 = ((int64_t)sg.b * p.n_pos + sg.i) * p.rows_b;
         const int32_t* idx_row = SPARSE ? p.indices + ((int64_t)sg.b * p.s_q + sg.i) * p.topk : nullptr;
 
         // Index word of tile k: sparse -> a VMEM load, lane l holds the raw index
@@ -182,11 +194,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             int row, dsub;
             if constexpr (R32) { row = 32 * ((VAR == kV64) ? (wave >> 1) : wave) + (ln & 31); dsub = 8 * (ln >> 5); }
             else { row = ln & 15; dsub = 8 * (ln >> 4); }
-            // Rows past h_q (padding of the last row group) load head 0's q:
-            // rows are independent and a padded row's output is never stored.
+            // Rows past the row space (padding of the last row group) load its
+            // row 0: rows are independent and a padded row's output is never stored.
             const int h = sg.h0 + row;
-            const uint16_t* qbase = p.q + qrow0 * F::kDqk;           // head 0 of this query position
-            const int qoff = (h < p.h_q ? h : 0) * F::kDqk + dsub;   // this lane's row and sub-block
+            const uint16_t* qbase = p.q + qrow0 * F::kDqk;              // row 0 of the row space
+            const int qoff = (h < p.rows_b ? h : 0) * F::kDqk + dsub;   // this lane's row and sub-block
             #pragma unroll
             for (int kk = 0; kk < NQ; ++kk) {
                 const int dim0 = R32 ? 16 * kk : 32 * kk;
@@ -202,12 +214,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         if (SPARSE) {
             T_q = (p.topk + kBlock - 1) / kBlock;
             sg.limit = p.topk;
+            sg.pos_lo = sg.i;
+            sg.k_cut = 0x7fffffff;
         } else {
             const int L = min(uniform(len_raw), kMaxSeqTokens);  // as the schedule reads it
             T_q = L > 0 ? (L + kBlock - 1) / kBlock : 0;
-            int lim = p.causal ? L - p.s_q + 1 + sg.i : L;
-            lim = min(lim, min(L, p.mbps * kBlock));
-            sg.limit = max(lim, 0);
+            // causal: position i sees L - s_q + 1 + i tokens. The unit's rows
+            // span positions pos_lo .. pos_hi (one position unless dense rows
+            // pack several); the tiles run to the last row's limit and
+            // tokens between the first and last row's limits are masked per row.
+            sg.pos_lo = sg.i;
+            int pos_hi = sg.i;
+            if (p.n_pos == 1) {
+                sg.pos_lo = sg.h0 / p.h_q;
+                pos_hi = (min(sg.h0 + RG, p.rows_b) - 1) / p.h_q;
+            }
+            const int cap = min(L, p.mbps * kBlock);
+            sg.limit = max(min(p.causal ? L - p.s_q + 1 + pos_hi : L, cap), 0);
+            const int lim_lo = max(min(p.causal ? L - p.s_q + 1 + sg.pos_lo : L, cap), 0);
+            sg.k_cut = 0x7fffffff;
+            if (MIXED && lim_lo != sg.limit) {
+                sg.k_cut = lim_lo / kBlock;   // first tile with tokens past the first row's limit
+                lds_cut[wave][0] = lim_lo;
+                lds_cut[wave][1] = sg.pos_lo;
+                lds_cut[wave][2] = sg.h0;
+            }
         }
         int t1 = (qq == qe) ? te : T_q - 1;
         sg.split = (qq == qb) ? fs : 0;
@@ -490,7 +521,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         // Side work between the score MFMAs (tile loads; see the tile
         // pipeline): side(j), j = 0 .. NQ/2 - 1, after the MFMAs of k-step 2 j
         // (j < NQ/2 - 1) or NQ - 3 (the last j), when the tag is true.
-        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, auto side_tag, auto&& side) {
+        // Row r's token limit relative to tile k, in a dense unit whose rows
+        // span positions: the first row's limit plus r's position offset.
+        auto row_cut = [&](int k, int r) -> int {
+            const int lim_lo = uniform(lds_cut[wave][0]), pos_lo = uniform(lds_cut[wave][1]);
+            const int h0 = uniform(lds_cut[wave][2]);
+            return lim_lo - k * kBlock + (h0 + r) / p.h_q - pos_lo;
+        };
+        auto compute_tile = [&](const char LDS_AS* tile, uint64_t mask, int k, auto side_tag, auto&& side) {
             constexpr bool kSideQk = decltype(side_tag)::value;
             if constexpr (R32) {
                 // S^T = K Q^T on 32x32x16 MFMAs: two accumulation chains (the two
@@ -549,6 +587,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                             const int t = 32 * tb + 8 * (v >> 2) + (v & 3);
                             if (!((mh >> t) & 1ull)) sc[bb][v] = -INFINITY;
                         }
+                    }
+                }
+                // a causal dense unit whose rows span positions: tokens past
+                // the first position's limit are masked per row
+                if (MIXED && k >= sg.k_cut) {
+                    const int ln2 = lane_fresh();
+                    const int rcut = row_cut(k, 32 * rw + (ln2 & 31)) - 4 * (ln2 >> 5);
+                    #pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int tb = (VAR == kV128) ? bb : tw;
+                        #pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            if (32 * tb + 8 * (v >> 2) + (v & 3) >= rcut) sc[bb][v] = -INFINITY;
                     }
                 }
                 float mt = sc[0][0];
@@ -646,6 +697,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     x[v] = s[v] * p.scale_log2;
                     const int t = 16 * wave + 4 * g + v;
                     if (!((mask >> t) & 1ull)) x[v] = -INFINITY;
+                }
+                // a causal dense unit whose rows span positions: tokens past
+                // the first position's limit are masked per row
+                if (MIXED && k >= sg.k_cut) {
+                    const int rcut = row_cut(k, lane_fresh() & 15);
+                    #pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (16 * wave + 4 * g + v >= rcut) x[v] = -INFINITY;
                 }
                 float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                 mt = fmaxf(mt, wave_shfl_xor(mt, 16));
@@ -748,7 +807,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 // chunk j is issued with the address computed after chunk j - 1,
                 // so its VALU fills the MFMA slots between the two loads
                 ChunkAddr ca = chunk_addr(0, tn);
-                compute_tile(tile, mask_a, std::true_type{}, [&](int j) {
+                compute_tile(tile, mask_a, k, std::true_type{}, [&](int j) {
                     if (j < F::kRawSlots) {
                         chunk_issue(j, cur, ca);
                         if (kDrainPipeline && j == F::kRawSlots - 1) wait_vm(0);
@@ -819,7 +878,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 const TileSrc tn = (k + 1 <= t1) ? tile_src(k + 1, idx_n) : none;
                 unsigned rows[2];
                 tile_rows(tn, rows);
-                compute_tile(cur, mask_a, std::true_type{}, [&](int j) {
+                compute_tile(cur, mask_a, k, std::true_type{}, [&](int j) {
                     qk_chunk(j, nxt, rows);
                     if (kDrainPipeline && j == 17) wait_vm(0);
                 });
@@ -865,9 +924,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                     if constexpr (kDrainPipeline) wait_vm(0);
-                    compute_tile(ctile, mask_a, std::false_type{}, [](int) {});
+                    compute_tile(ctile, mask_a, k, std::false_type{}, [](int) {});
                 } else {
-                    compute_tile(cur, mask_a, std::false_type{}, [](int) {});
+                    compute_tile(cur, mask_a, k, std::false_type{}, [](int) {});
                     block_sync_lds();
                     if (k + 2 <= t1) mask_c = issue_tile(kLooped, k + 2, cur, idx_c);
                     if constexpr (kDrainPipeline) wait_vm(0);
@@ -958,16 +1017,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                     #pragma unroll 4
                     for (int r = 0; r < 32; ++r) {
                         const int hr = sg.h0 + 32 * rw + r;
-                        if (hr < p.h_q && 4 * ln < kHalfD) {
+                        if (hr < p.rows_b && 4 * ln < kHalfD) {
                             const i16x4 w = *(const i16x4 LDS_AS*)(stg + r * kStg + 4 * ln);
                             *(i16x4*)(p.o + (qrow0 + hr) * F::kDv + half * kHalfD + 4 * ln) = w;
                         }
                     }
                 }
-                if (hh == 0 && h < p.h_q) p.lse[qrow0 + h] = lse_v;
+                if (hh == 0 && h < p.rows_b) p.lse[qrow0 + h] = lse_v;
                 block_sync_lds();  // every wave has read its staged rows before the next segment's loads
             } else if (final_out) {
-                if (h < p.h_q) {
+                if (h < p.rows_b) {
                     uint16_t* op = p.o + (qrow0 + h) * F::kDv;
                     #pragma unroll
                     for (int d = 0; d < NO; ++d) {
@@ -1059,7 +1118,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
                 for (int j = 0; j < NJ; ++j) acc[j] += ew * *(const f32x4 LDS_AS*)(mo + (w * 16 + mr) * kMoStride + c4 + 64 * j);
             }
             if (final_out) {
-                if (h < p.h_q) {
+                if (h < p.rows_b) {
                     uint16_t* op = p.o + (qrow0 + h) * F::kDv + c4;
                     #pragma unroll
                     for (int j = 0; j < NJ; ++j) {
@@ -1096,17 +1155,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     }
 }
 
-template <int FMT, bool SPARSE, int VAR>
-hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<FMT, SPARSE, VAR>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
+template <int FMT, int VAR>
+hipError_t launch_one(const DecodeParams& p, bool sparse, bool mixed, hipStream_t s) {
+    if (sparse)
+        hipLaunchKernelGGL((decode_kernel<FMT, true, VAR, false>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
+    else if (mixed)
+        hipLaunchKernelGGL((decode_kernel<FMT, false, VAR, true>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<FMT, false, VAR, false>), dim3(p.num_parts), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_format(const DecodeParams& p, int variant, bool sparse, hipStream_t s) {
-    if (variant == kV128) return sparse ? launch_one<FMT, true, kV128>(p, s) : launch_one<FMT, false, kV128>(p, s);
-    if (variant == kV64) return sparse ? launch_one<FMT, true, kV64>(p, s) : launch_one<FMT, false, kV64>(p, s);
-    return sparse ? launch_one<FMT, true, kV16>(p, s) : launch_one<FMT, false, kV16>(p, s);
+    // A dense causal call packs s_q positions of h_q rows into one row space;
+    // a group of rg rows straddles two positions exactly when h_q is not a
+    // multiple of rg (the group holding rows h_q - 1 and h_q).
+    const int rg = (variant == kV128) ? 128 : (variant == kV64 ? 64 : 16);
+    const bool mixed = !sparse && p.causal && p.s_q > 1 && p.h_q % rg != 0;
+    if (variant == kV128) return launch_one<FMT, kV128>(p, sparse, mixed, s);
+    if (variant == kV64) return launch_one<FMT, kV64>(p, sparse, mixed, s);
+    return launch_one<FMT, kV16>(p, sparse, mixed, s);
 }
 
 }  // namespace

@@ -9,10 +9,16 @@ splits each processor part takes. The pages give no format or balancing rule,
 so this is the library's own documented rule, written here as a per-tile
 assignment (the GPU computes the same result per part, in parallel):
 
-  * Work units are "row-group sequences" q = b * n_rg + rg, rg = i * n_hb + hb
-    (query position i, head block hb of rg_rows heads). Unit q has T_q tiles
-    of 64 tokens: ceil(L_b / 64) dense, ceil(topk / 64) sparse, with L_b read
-    as at most 2^23 (the longest sequence a call attends).
+  * The query rows of sequence b are its rows of q in order, (position i,
+    head h) -> i * h_q + h. A dense call puts all s_q * h_q of them in one
+    row space, since every position reads the same cache ([Walkthrough] §七
+    "先算清楚瓶颈" counts a request's h_q * s_q query rows against one pass
+    over the KV); a sparse call has one row space of h_q rows per position, each with
+    its own indices. Work units are "row-group sequences" q = b * n_rg + rg,
+    rg = i * n_hb + hb (row space i, block hb of rg_rows consecutive rows).
+    Unit q has T_q tiles of 64 tokens: ceil(L_b / 64) dense, ceil(topk / 64)
+    sparse, with L_b read as at most 2^23 (the longest sequence a call
+    attends).
   * Units are laid end to end on a line; a non-empty unit first takes
     fixed_cost positions (its per-split overhead), then one position per tile.
   * With total = sum over non-empty units of (fixed_cost + T_q) and
@@ -41,8 +47,10 @@ MAX_SEQ_TOKENS = 1 << 23
 def tile_counts(cache_seqlens: Optional[Sequence[int]], batch: int, s_q: int, h_q: int,
                 topk: int, rg_rows: int) -> List[int]:
     """T_q for every row-group sequence, in q order."""
-    n_hb = -(-h_q // rg_rows)
-    n_rg = s_q * n_hb
+    rows = h_q if topk > 0 else s_q * h_q   # rows of one row space
+    n_pos = s_q if topk > 0 else 1           # row spaces per sequence
+    n_hb = -(-rows // rg_rows)
+    n_rg = n_pos * n_hb
     out = []
     for b in range(batch):
         L = min(max(int(cache_seqlens[b]), 0), MAX_SEQ_TOKENS)

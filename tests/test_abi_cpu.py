@@ -72,6 +72,24 @@ def test_sizes():
     assert ws == ((slots * 128 * 512 * 2 + 255) // 256) * 256 + 2 * slots * 128 * 4
 
 
+def _ws(slots, rg):
+    return ((slots * rg * 512 * 2 + 255) // 256) * 256 + 2 * slots * rg * 4
+
+
+def test_sizes_cover_dense_and_sparse_row_spaces():
+    # s_q = 2, h_q = 16: a dense call packs 32 rows per sequence (one 64-row
+    # group); a sparse call has two 16-row groups, one per position
+    assert m.metadata_size(16, 2, 16, 256) == (256 * 8, 16 * 2 + 1)
+    assert m.workspace_size(16, 2, 16, 256) == max(_ws(16 + 256, 64), _ws(32 + 256, 16))
+    # s_q = 4, h_q = 32: dense 128 rows = one 128-row group; sparse 4 x one 64-row group
+    assert m.metadata_size(8, 4, 32, 64) == (64 * 8, 8 * 4 + 1)
+    assert m.workspace_size(8, 4, 32, 64) == max(_ws(8 + 64, 128), _ws(32 + 64, 64))
+    # the sparse shape exceeds the unit limit (4096 x 4 groups), the dense one fits:
+    # the sizes are the dense call's
+    assert m.metadata_size(4096, 4, 16, 256) == (256 * 8, 4096 + 1)
+    assert m.workspace_size(4096, 4, 16, 256) == _ws(4096 + 256, 64)
+
+
 @pytest.mark.parametrize("bad", [dict(batch=0), dict(s_q=0), dict(h_q=0), dict(num_parts=0), dict(num_parts=70000)])
 def test_size_queries_reject_bad_shapes(bad):
     kw = dict(batch=4, s_q=1, h_q=128, num_parts=256)

@@ -47,9 +47,11 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     split that read beyond the chunk would turn its zero weight into NaN."""
     say(f"combine h_q={h_q} s_q={s_q} parts={P} splits<{max_splits}")
     dev = "cuda:0"
-    RG = 16 if h_q <= 16 else (64 if h_q <= 64 else 128)
-    n_hb = -(-h_q // RG)
-    n_rg = s_q * n_hb
+    # a dense call: all s_q * h_q rows of a sequence in one row space
+    R = s_q * h_q
+    RG = 16 if R <= 16 else (64 if R <= 64 else 128)
+    n_hb = -(-R // RG)
+    n_rg = n_hb
     Q = B * n_rg
     rng = np.random.default_rng(h_q + s_q)
     n_splits = rng.integers(0, max_splits, Q)
@@ -91,20 +93,25 @@ def test_combine_matches_oracle_merge(B, h_q, s_q, P, max_splits):
     bt = torch.zeros((B, 1), dtype=torch.int32, device=dev)
     seq = torch.zeros((B,), dtype=torch.int32, device=dev)
     tm = torch.zeros((P, 8), dtype=torch.int32, device=dev)
-    so = torch.from_numpy(offs).to(dev)
+    # the split-offset buffer has the size the size query gives (it covers a
+    # sparse call of this shape too); the merge reads the first Q + 1
+    _, n_off = mla.metadata_size(B, s_q, h_q, P)
+    so_full = np.zeros(n_off, dtype=np.int32)
+    so_full[:Q + 1] = offs
+    so = torch.from_numpy(so_full).to(dev)
     a = mla.make_args(q, kv, bt, seq, tm, so, 0.1, False, False, None, ws, o, lse)
     mla.mla_combine(a, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     og = o.float().cpu().numpy()
     lg = lse.cpu().numpy()
     for qq in range(Q):
-        b, rgi = divmod(qq, n_rg)
-        i, hb = divmod(rgi, n_hb)
+        b, hb = divmod(qq, n_rg)
         n = n_splits[qq]
         for r in range(RG):
-            h = hb * RG + r
-            if h >= h_q:
+            f = hb * RG + r          # row of the row space: position f // h_q, head f % h_q
+            if f >= R:
                 continue
+            i, h = divmod(f, h_q)
             if n == 1:
                 assert np.all(og[b, i, h] == 7.0) and lg[b, i, h] == 7.0   # left for the split kernel
                 continue

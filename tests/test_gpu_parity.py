@@ -60,6 +60,30 @@ SMALL = [
                                                    sparse_tokens_per_seq=512, prefix_sparse=True)),
     ("fp8 sparse prefill chunk h16 s_q=33", dict(batch=1, s_q=33, h_q=16, kv_format="fp8", topk=100,
                                                  sparse_tokens_per_seq=256, prefix_sparse=True, invalid_frac=0.1)),
+    # dense calls pack all s_q * h_q rows of a sequence into one row space:
+    # row groups that hold several positions (each with its own causal limit),
+    # positions cut across row-group boundaries, a position with no token
+    ("bf16 causal s_q=2 h16 packed, L < s_q", dict(batch=3, s_q=2, h_q=16, seqlens=[1, 2, 300], kv_format="bf16",
+                                                    causal=True)),
+    ("bf16 causal s_q=8 h16 packed 128 rows", dict(batch=3, s_q=8, h_q=16, seqlens=[64, 65, 63], kv_format="bf16",
+                                                    causal=True)),
+    ("fp8 causal s_q=2 h64 packed", dict(batch=2, s_q=2, h_q=64, seqlens=[700, 129], kv_format="fp8", causal=True)),
+    ("bf16 causal s_q=3 h100 positions across groups", dict(batch=2, s_q=3, h_q=100, seqlens=[190, 5],
+                                                              kv_format="bf16", causal=True)),
+    ("bf16 dense s_q=2 h16 packed, not causal", dict(batch=2, s_q=2, h_q=16, seqlens=[640, 77], kv_format="bf16")),
+    ("fp8_528 causal s_q=5 h4 packed", dict(batch=2, s_q=5, h_q=4, seqlens=[260, 4], kv_format="fp8_528",
+                                            causal=True)),
+    # position-spanning row groups in every format and row-group size
+    ("bf16 causal s_q=4 h4 packed 16 rows", dict(batch=2, s_q=4, h_q=4, seqlens=[333, 3], kv_format="bf16",
+                                                 causal=True)),
+    ("fp8 causal s_q=2 h8 packed 16 rows", dict(batch=2, s_q=2, h_q=8, seqlens=[129, 64], kv_format="fp8",
+                                                causal=True)),
+    ("fp8 causal s_q=3 h16 packed 48 rows", dict(batch=2, s_q=3, h_q=16, seqlens=[500, 66], kv_format="fp8",
+                                                 causal=True)),
+    ("fp8_528 causal s_q=3 h5 packed 15 rows", dict(batch=2, s_q=3, h_q=5, seqlens=[191, 2], kv_format="fp8_528",
+                                                    causal=True)),
+    ("fp8_528 causal s_q=2 h96 packed 192 rows", dict(batch=2, s_q=2, h_q=96, seqlens=[450, 128],
+                                                      kv_format="fp8_528", causal=True)),
     # 528-byte rows: 512-dim keys, 448-dim values, UE8M0 scales per 32 values
     ("fp8_528 dense h128 ragged", dict(batch=3, s_q=1, h_q=128, seqlens=[1, 130, 700], kv_format="fp8_528")),
     ("fp8_528 dense h16 ragged", dict(batch=4, s_q=1, h_q=16, seqlens=[64, 65, 1000, 3], kv_format="fp8_528")),
@@ -131,3 +155,7 @@ def test_config8_fp8_528_causal_all_rows():
 
 def test_config9_sparse_fp8_528_all_rows():
     _check(config_workload(9), label="config 9 (528-byte rows, sparse, all rows)")
+
+
+def test_config10_two_position_low_head_all_rows():
+    _check(config_workload(10), label="config 10 (two positions packed, causal, all rows)")

@@ -8,8 +8,8 @@ instruction, so with the same schedule the outputs must be equal bit for bit;
 a load issued into a buffer that some wave still reads would make them differ.
 Every pipeline is covered: FP8 with 128-row groups (loads between the score
 MFMAs, sparse index ring), bf16 with 128-row groups, and the 64- and 16-row
-groups' two-tiles-ahead pipeline, dense and sparse, each over segments of
-many tiles."""
+groups' two-tiles-ahead pipeline, dense (with and without row groups that
+span query positions) and sparse, each over segments of many tiles."""
 
 import ctypes
 
@@ -34,6 +34,8 @@ CASES = [
     ("bf16", 64, 2, True, False),
     ("fp8", 64, 1, False, True),
     ("bf16", 16, 1, False, False),
+    ("bf16", 8, 2, True, False),
+    ("fp8", 16, 3, True, False),
     ("fp8_528", 16, 2, True, True),
 ]
 

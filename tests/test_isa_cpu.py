@@ -20,7 +20,7 @@ LLVM = "/opt/rocm/llvm/bin"
 TOOLS = ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 TARGET = f"hipv4-amdgcn-amd-amdhsa--{B.ARCH}"
-KERNEL_RE = re.compile(r"decode_kernelILi(\d)ELb(\d)ELi(\d)E")
+KERNEL_RE = re.compile(r"decode_kernelILi(\d)ELb(\d)ELi(\d)ELb(\d)E")
 # k-steps of 16 key dims per 32-row MFMA block: the q loads of a row group
 NQ = {1: 576 // 16, 2: 512 // 16}
 VMEM_LOAD = re.compile(r"^(global_load|buffer_load|flat_load)")
@@ -34,7 +34,7 @@ def functions():
 
 
 def _decode_functions(lib):
-    """{(format, sparse, variant): [(address, instruction, branch target)]} of the decode kernels."""
+    """{(format, sparse, variant, mixed): [(address, instruction, branch target)]} of the decode kernels."""
     for t in TOOLS:
         if not os.path.exists(os.path.join(LLVM, t)):
             pytest.skip(f"{t} not found")
@@ -69,7 +69,8 @@ def _decode_functions(lib):
             funcs[cur].append((int(i.group(2), 16), i.group(1), target))
     decode = {tuple(int(x) for x in KERNEL_RE.search(n).groups()): body
               for n, body in funcs.items() if KERNEL_RE.search(n)}
-    assert len(decode) == 18, sorted(decode)  # 3 formats x dense/sparse x 3 row-group sizes
+    # 3 formats x (dense, dense with position-spanning row groups, sparse) x 3 row-group sizes
+    assert len(decode) == 27, sorted(decode)
     return decode
 
 
@@ -101,7 +102,7 @@ def test_sparse_ring_wait_counts_only_later_loads(functions, fmt):
     loads the compiler does not track, then waits with vmcnt(NQ) before reading
     them: that is only sound if at least NQ VMEM loads (the q loads) are
     issued between the third ring load and the wait."""
-    body = functions[(fmt, 1, 0)]
+    body = functions[(fmt, 1, 0, 0)]
     ring = [i for i, (_, ins, _) in enumerate(body) if re.match(r"^buffer_load_dword\s.*\blds\b", ins)]
     assert len(ring) >= 3
     third = ring[2]

@@ -72,6 +72,11 @@ def test_tile_counts_layout():
     assert tile_counts([130], 1, 1, 20, 0, 16) == [3, 3]
     # sparse ignores cache_seqlens
     assert tile_counts([5, 5], 2, 1, 128, 2048, 128) == [32, 32]
+    # dense calls pack the s_q positions of a sequence into one row space
+    # (s_q * h_q rows), sparse calls keep one row space per position
+    assert tile_counts([100, 200], 2, 2, 16, 0, 64) == [2, 4]
+    assert tile_counts([100, 200], 2, 2, 16, 2048, 16) == [32] * 4
+    assert tile_counts([130], 1, 4, 40, 0, 128) == [3, 3]
 
 
 @pytest.mark.parametrize("seed", range(10))

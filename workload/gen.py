@@ -46,6 +46,7 @@ CONFIG_NAMES = {
     7: "dense bf16 64-head share: B=16 s_q=1 h_q=64 L~U[1024,4096]",
     8: "fp8_528 paged causal: B=64 s_q=2 h_q=128 L=8192",
     9: "sparse fp8_528: B=32 s_q=1 h_q=128 topk=2048 (5% -1)",
+    10: "low-head two-position causal bf16: B=16 s_q=2 h_q=16 L=65536",
 }
 
 
@@ -251,8 +252,9 @@ def make_workload(
 
 
 def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
-    """The five decode workloads, the sparse prefill chunk (6), the 64-head share (7) and the two FP8 shapes
-    with 528-byte rows (8, 9); config 3 takes its fixed sequence length."""
+    """The five decode workloads, the sparse prefill chunk (6), the 64-head share (7), the two FP8 shapes
+    with 528-byte rows (8, 9) and the two-position low-head share (10); config 3 takes its fixed sequence
+    length."""
     if cfg == 1:
         # q and cache drawn in fp32 then rounded to bf16; 4 pages, shuffled.
         return make_workload(batch=1, s_q=1, h_q=4, seqlens=[256], kv_format="bf16",
@@ -286,4 +288,9 @@ def config_workload(cfg: int, seqlen: int = 8192, seed: int = 0) -> Workload:
         # the sparse FP8 shape with 528-byte rows
         return make_workload(batch=32, s_q=1, h_q=128, kv_format="fp8_528", topk=2048,
                              sparse_tokens_per_seq=32768, invalid_frac=0.05, seed=seed, name=CONFIG_NAMES[9])
+    if cfg == 10:
+        # the low-head share with two query positions per sequence (a draft
+        # token verified with the next one): 32 rows attend one cache
+        return make_workload(batch=16, s_q=2, h_q=16, seqlens=[65536] * 16, kv_format="bf16",
+                             causal=True, seed=seed, name=CONFIG_NAMES[10])
     raise ValueError(f"unknown config {cfg}")
