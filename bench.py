@@ -67,8 +67,34 @@ KERNEL_SOURCES = ("mla_decode.hip", "mla_device.h", "mla_common.h")
 QUANT_SOURCES = ("mla_quantize.hip", "mla_quantize.h", "mla_common.h")
 
 
+def code_without_comments(text: str) -> str:
+    """C/C++ source with its comments and blank lines removed (string and character literals kept
+    as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
+
+
 def source_hash(names=KERNEL_SOURCES, compiled="mla_decode.hip") -> str:
-    """sha256 over a kernel's sources and its compile flags (first 16 hex digits).
+    """sha256 over a kernel's sources without their comments and its compile flags (first 16 hex
+    digits), so that a change to comments alone keeps the value.
 
     Include paths are left out of the flags so the value does not depend on where the tree sits.
     """
@@ -78,8 +104,8 @@ def source_hash(names=KERNEL_SOURCES, compiled="mla_decode.hip") -> str:
 
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(B.CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(B.CSRC, name), encoding="utf-8") as f:
+            h.update(code_without_comments(f.read()).encode())
     flags = B.COMMON_FLAGS + B.EXTRA_FLAGS.get(compiled, [])
     kept = [f for i, f in enumerate(flags) if f != "-I" and not (i > 0 and flags[i - 1] == "-I")]
     h.update("\0".join(kept).encode())

@@ -1,8 +1,10 @@
 // MLA decode split kernel for gfx950 (CDNA4), plus its launcher.
 //
 // What it computes ([Walkthrough] §六 "结果：decode 变成 MQA", §五 "公式";
-// §七 "split-KV"): for each row group (RG query heads of one query position
-// of one sequence) and a contiguous range of 64-token tiles, the online-
+// §七 "split-KV"): for each row group (RG consecutive query rows of one
+// sequence: rows (position i, head h) -> i * h_q + h of all its positions
+// when dense, since they all read the same cache, or the heads of one
+// position when sparse) and a contiguous range of 64-token tiles, the online-
 // softmax attention state (running max m, running sum l, unnormalised output
 // O) over those tokens; then either the final o = O / l and lse, or the
 // normalised partial (O / l, lse) for the split merge.

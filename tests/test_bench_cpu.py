@@ -106,3 +106,14 @@ def test_absorb_counts_and_traffic_rows():
     rows = {r[2]: int(r[3]) for r in rows if len(r) == 5 and r[0] == "traffic" and r[1] == name}
     for kern, algo in (("absorb_q", ba), ("unabsorb_o", bu)):
         assert algo <= rows[kern] < 1.05 * algo
+
+
+def test_source_hash_ignores_comments_only():
+    """The kernel sources hash keys the committed counter rows: an edit to comments or blank lines
+    keeps it, any change to the code (string literals included) moves it."""
+    code = 'int a = 1; // note\n/* block\n comment */ const char* s = "x // y /* z */";\n\nint b;\n'
+    same = '// header\nint a = 1;\n\n  const char* s = "x // y /* z */";   // trailing\nint b;'
+    assert bench.code_without_comments(code) == bench.code_without_comments(same)
+    assert bench.code_without_comments(code) != bench.code_without_comments(code.replace("b;", "c;"))
+    assert bench.code_without_comments(code) != bench.code_without_comments(code.replace("// y", "// w"))
+    assert bench.code_without_comments("char c = '\\'';  // q\nint d;") == "char c = '\\'';\nint d;"
