@@ -74,9 +74,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
     // other variants use one array (the 64- and 16-head ones reuse all of it
     // for their end-of-segment merge).
     constexpr bool kFp8Pipe = FP8 && VAR == kV128;
-    // bf16 with 128-head groups (dense or sparse) issues each tile's loads
-    // between the score MFMAs of the tile before it (see the tile pipeline).
-    constexpr bool kQkLoads = !FP8 && VAR == kV128;
+    // bf16 with 128- or 64-row groups (dense or sparse) issues each tile's
+    // loads between the score MFMAs of the tile before it (see the tile
+    // pipeline).
+    constexpr bool kQkLoads = !FP8 && (VAR == kV128 || VAR == kV64);
     // Every dense variant reads block-table words as scalar loads and issues
     // its tile loads as inline asm the compiler does not track, so that no
     // compiler wait for a load in flight lands inside the tile loop (in the

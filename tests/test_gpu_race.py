@@ -7,8 +7,9 @@ somewhere during tile k. The arithmetic is the same instruction for
 instruction, so with the same schedule the outputs must be equal bit for bit;
 a load issued into a buffer that some wave still reads would make them differ.
 Every pipeline is covered: FP8 with 128-row groups (loads between the score
-MFMAs, sparse index ring), bf16 with 128-row groups, and the 64- and 16-row
-groups' two-tiles-ahead pipeline, dense (with and without row groups that
+MFMAs, sparse index ring), bf16 with 128- and 64-row groups (loads between the
+score MFMAs), and the two-tiles-ahead pipeline of FP8 with 64-row groups and
+of 16-row groups, dense (with and without row groups that
 span query positions) and sparse, each over segments of many tiles."""
 
 import ctypes
@@ -32,6 +33,8 @@ CASES = [
     ("fp8_528", 128, 1, True, False),
     ("fp8_528", 128, 1, False, True),
     ("bf16", 64, 2, True, False),
+    ("bf16", 32, 1, False, False),
+    ("bf16", 64, 1, False, True),
     ("fp8", 64, 1, False, True),
     ("bf16", 16, 1, False, False),
     ("bf16", 8, 2, True, False),
