@@ -36,6 +36,8 @@ CASES = [
     ("bf16", 32, 1, False, False),
     ("bf16", 64, 1, False, True),
     ("fp8", 64, 1, False, True),
+    ("fp8_528", 48, 1, False, False),
+    ("fp8_528", 32, 1, False, True),
     ("bf16", 16, 1, False, False),
     ("bf16", 8, 2, True, False),
     ("fp8", 16, 3, True, False),
