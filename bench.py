@@ -158,6 +158,84 @@ def copy_probe(mib: int, reps: int):
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
 
 
+PROBE_MFMA_ITERS = 20000      # ~4 ms per launch on the whole chip
+PROBE_READ_BYTES = 2 << 30    # 2 GiB: eight times the Infinity Cache
+
+
+def achievable_peaks(stream, reps: int = 7, read_blocks_per_cu=(1, 2, 4, 8)):
+    """What this GPU reaches on its own, beside the published peaks (context for the roofline fractions).
+
+    MFMA: the library's MFMA loop (four independent 32x32x16 bf16 chains per wave, register operands,
+    four workgroups of four waves per CU). HBM: the library's read probe over 2 GiB with non-temporal
+    16-byte loads (each workgroup a contiguous range), the best of a few grid sizes. Each figure is the median of `reps` launches timed
+    with HIP events on `stream`, after two untimed ones.
+    """
+    import statistics
+
+    import torch
+
+    import mla_latent_kv_10_amd as mla
+
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn):
+        times = []
+        with torch.cuda.stream(stream):
+            for i in range(reps + 2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                if i >= 2:
+                    times.append(e0.elapsed_time(e1))
+        return statistics.median(times)
+
+    blocks = 4 * n_cu
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ms = timed(lambda: mla.probe_mfma_bf16(PROBE_MFMA_ITERS, blocks, 1.0, sink))
+    want = 1024.0 * PROBE_MFMA_ITERS
+    if not bool(torch.all(sink == want)):
+        raise RuntimeError("MFMA probe returned a wrong sum")
+    mfma_tflops = blocks * 4 * PROBE_MFMA_ITERS * 4 * 32768 / (ms * 1e-3) / 1e12
+    del sink
+    src = torch.empty(PROBE_READ_BYTES // 4, dtype=torch.int32, device=dev)
+    src.random_(-(2 ** 31), 2 ** 31 - 1)
+    best = None
+    for per_cu in read_blocks_per_cu:
+        rb = per_cu * n_cu
+        rsink = torch.empty(rb * 256, dtype=torch.int32, device=dev)
+        ms_r = timed(lambda: mla.probe_hbm_read(src, rb, rsink))
+        if best is None or ms_r < best[0]:
+            best = (ms_r, per_cu)
+    read_gbps = PROBE_READ_BYTES / (best[0] * 1e-3) / 1e9
+    del src
+    torch.cuda.synchronize()
+    return {"hbm_read_GBps": round(read_gbps, 1), "hbm_read_frac_of_spec": round(read_gbps / HBM_PEAK_GBPS, 4),
+            "mfma_bf16_TFLOPS": round(mfma_tflops, 1), "mfma_frac_of_spec": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+            "method": f"HBM: one read of 2 GiB with non-temporal 16-byte loads, {best[1]} workgroups of 256 threads "
+                      f"per CU, each a contiguous range; MFMA: four 32x32x16 bf16 chains per wave on register operands, {blocks} workgroups "
+                      f"of 4 waves; medians of {reps} launches"}
+
+
+def add_achievable_fracs(out: dict, peaks: dict) -> None:
+    """Beside each roofline fraction (against the published peak), the same figure against the measured one."""
+    def one(r):
+        if not r:
+            return
+        ref = peaks["hbm_read_GBps"] if r.get("bound") == "hbm" else peaks["mfma_bf16_TFLOPS"]
+        r["frac_of_achievable"] = round(r["achieved"] / ref, 4)
+
+    one(out.get("roofline"))
+    for e in out.get("sweep", []):
+        one(e.get("roofline"))
+    for e in out.get("configs", {}).values():
+        one(e.get("roofline"))
+    for e in out.get("ops", {}).values():
+        one(e.get("roofline"))
+
+
 def build_workload(args):
     from workload import config_workload
 
@@ -604,9 +682,10 @@ def main():
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("decode", "quantize", "absorb"), default="decode",
+    ap.add_argument("--op", choices=("decode", "quantize", "absorb", "peaks"), default="decode",
                     help="decode: the decode step (default); quantize: the FP8 cache writer; "
-                         "absorb: the absorption products around the decode")
+                         "absorb: the absorption products around the decode; peaks: only the measured "
+                         "achievable HBM read and bf16 MFMA rates")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -628,6 +707,10 @@ def main():
         return
     if args.op == "absorb":
         bench_absorb(args)
+        return
+    if args.op == "peaks":
+        print(json.dumps({"achievable": achievable_peaks(torch.cuda.Stream(device=torch.device("cuda:0")))}),
+              flush=True)
         return
     num_parts = args.num_parts or mla.default_num_parts(0)
     stream = torch.cuda.Stream(device=torch.device("cuda:0"))
@@ -709,6 +792,11 @@ def main():
                       "absorb": {k: v for k, v in bench_absorb(side, emit=False).items()
                                  if k in keep + ("absorb_q_ms", "unabsorb_o_ms", "tflops")}}
         progress(f"ops: quantize {out['ops']['quantize']['value']} GB/s, absorb {out['ops']['absorb']['value']} GB/s")
+        # measured achievable peaks, for context beside the published ones
+        out["achievable"] = achievable_peaks(stream)
+        add_achievable_fracs(out, out["achievable"])
+        progress(f"achievable: {out['achievable']['hbm_read_GBps']} GB/s read, "
+                 f"{out['achievable']['mfma_bf16_TFLOPS']} TFLOP/s bf16 MFMA")
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_seconds)
         cb["cpu_model"] = cpu_model()

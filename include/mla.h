@@ -291,6 +291,31 @@ int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, int
  */
 int mla_unabsorb_o(const void* o_latent, const void* w_uv, int64_t tokens, int heads, void* out, void* stream);
 
+/*
+ * Measurement aids, not part of the decode path: what this GPU reaches on its
+ * own, reported beside the published peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16
+ * MFMA) that the decode's roofline fractions are taken against.
+ *
+ * mla_probe_mfma_bf16: `blocks` workgroups of four wave64s; every wave runs
+ *   `iters` steps of four independent v_mfma_f32_32x32x16_bf16 accumulation
+ *   chains on register operands whose elements all equal bf16(value). FLOPs
+ *   per launch: blocks * 4 * iters * 4 * 32768.
+ *   sink  device float [blocks * 256], written: per thread the sum of its 64
+ *         accumulator values, 1024 * iters * bf16(value)^2 in exact
+ *         arithmetic (exact in fp32 while that stays below 2^24).
+ * mla_probe_hbm_read: reads `bytes` of src once, with non-temporal 16-byte
+ *   loads from `blocks` workgroups of 256 threads.
+ *   src   device, 16-byte aligned, bytes a positive multiple of 16; read only.
+ *   sink  device uint32 [blocks * 256], written: per thread the sum modulo
+ *         2^32 of the 32-bit words it read (the sum over all threads is the
+ *         sum of every word of src).
+ * Errors: MLA_ERR_INVALID (iters < 1, blocks outside [1, 2^20], NULL or
+ * misaligned pointers, bytes not a positive multiple of 16), MLA_ERR_HIP
+ * (launch failure). Asynchronous on `stream`; allocate nothing.
+ */
+int mla_probe_mfma_bf16(int iters, int blocks, float value, float* sink, void* stream);
+int mla_probe_hbm_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

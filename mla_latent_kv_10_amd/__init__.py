@@ -83,6 +83,8 @@ EXPORTS = (
     "mla_quantize_fp8_append",
     "mla_absorb_q",
     "mla_unabsorb_o",
+    "mla_probe_mfma_bf16",
+    "mla_probe_hbm_read",
 )
 
 _lib = None
@@ -128,6 +130,8 @@ def _load(path: str) -> ctypes.CDLL:
                                ctypes.c_void_p, ctypes.c_void_p]
     L.mla_unabsorb_o.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                  ctypes.c_void_p]
+    L.mla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.mla_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     for name in EXPORTS:
         getattr(L, name).restype = ctypes.c_char_p if name == "mla_last_error" else ctypes.c_int
     return L
@@ -398,3 +402,33 @@ def unabsorb_o(o_latent, w_uv):
                                _stream_handle(o_latent.device)))
     return out
 
+
+
+# ---------------------------------------------------------------- measurement aids
+
+
+def probe_mfma_bf16(iters: int, blocks: int, value: float, sink) -> None:
+    """Enqueue the MFMA loop (blocks x 4 waves x iters x 4 MFMAs of 32x32x16 bf16) on the current stream.
+
+    sink: float32 [blocks * 256] on the GPU, receives 1024 * iters * bf16(value)^2 per thread.
+    """
+    torch = _torch()
+    _require_gpu(sink)
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must be float32 with at least blocks * 256 elements")
+    check(lib().mla_probe_mfma_bf16(iters, blocks, value, sink.data_ptr(), _stream_handle(sink.device)))
+
+
+def probe_hbm_read(src, blocks: int, sink) -> None:
+    """Enqueue one non-temporal read of every byte of src (a multiple of 16 bytes) on the current stream.
+
+    sink: int32 [blocks * 256] on the GPU, receives per thread the sum mod 2^32 of the words it read.
+    """
+    torch = _torch()
+    _require_gpu(src, sink)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if sink.dtype != torch.int32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must be int32 with at least blocks * 256 elements")
+    nbytes = src.numel() * src.element_size()
+    check(lib().mla_probe_hbm_read(src.data_ptr(), nbytes, blocks, sink.data_ptr(), _stream_handle(src.device)))

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # right after issuing them (MLA_DRAIN_PIPELINE): the LDS race check compares
 # its outputs with the pipelined library's, bit for bit.
 DRAIN_LIB_PATH = os.path.join(HERE, "libmla_mi355x_drain.so")
-SOURCES = ["mla_abi.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_combine.hip", "mla_quantize.hip", "mla_absorb.hip"]
+SOURCES = ["mla_abi.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_combine.hip", "mla_quantize.hip", "mla_absorb.hip",
+           "mla_probe.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -10,6 +10,7 @@
 
 #include "mla.h"
 #include "mla_common.h"
+#include "mla_probe.h"
 #include "mla_quantize.h"
 #include "mla_absorb.h"
 
@@ -347,6 +348,25 @@ int mla_quantize_fp8_append(const void* src, const int32_t* slots, int64_t n, vo
     p.num_rows = (int)(num_blocks * mla::kBlock);
     hipError_t e = mla::launch_quantize(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_probe_mfma_bf16(int iters, int blocks, float value, float* sink, void* stream) {
+    if (iters < 1) return fail(MLA_ERR_INVALID, "iters must be >= 1 (got %d)", iters);
+    if (blocks < 1 || blocks > (1 << 20)) return fail(MLA_ERR_INVALID, "blocks must be in [1, 2^20] (got %d)", blocks);
+    if (!sink || !aligned(sink, 4)) return fail(MLA_ERR_INVALID, "sink must be non-NULL and 4-byte aligned");
+    hipError_t e = mla::launch_probe_mfma(iters, blocks, value, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_probe_hbm_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, void* stream) {
+    if (bytes < 16 || bytes % 16 != 0) return fail(MLA_ERR_INVALID, "bytes must be a positive multiple of 16");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(MLA_ERR_INVALID, "blocks must be in [1, 2^20] (got %d)", blocks);
+    if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4))
+        return fail(MLA_ERR_INVALID, "src must be non-NULL and 16-byte aligned, sink non-NULL and 4-byte aligned");
+    hipError_t e = mla::launch_probe_hbm_read(src, bytes, blocks, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
     return ok();
 }
 

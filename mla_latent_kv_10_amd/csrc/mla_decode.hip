@@ -217,7 +217,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
         if (SPARSE) {
             T_q = (p.topk + kBlock - 1) / kBlock;
             sg.limit = p.topk;
-            sg.pos_lo = sg.i;
             sg.k_cut = 0x7fffffff;
         } else {
             const int L = min(uniform(len_raw), kMaxSeqTokens);  // as the schedule reads it
@@ -226,20 +225,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             // span positions pos_lo .. pos_hi (one position unless dense rows
             // pack several); the tiles run to the last row's limit and
             // tokens between the first and last row's limits are masked per row.
-            sg.pos_lo = sg.i;
-            int pos_hi = sg.i;
+            int pos_lo = sg.i, pos_hi = sg.i;
             if (p.n_pos == 1) {
-                sg.pos_lo = sg.h0 / p.h_q;
+                pos_lo = sg.h0 / p.h_q;
                 pos_hi = (min(sg.h0 + RG, p.rows_b) - 1) / p.h_q;
             }
             const int cap = min(L, p.mbps * kBlock);
             sg.limit = max(min(p.causal ? L - p.s_q + 1 + pos_hi : L, cap), 0);
-            const int lim_lo = max(min(p.causal ? L - p.s_q + 1 + sg.pos_lo : L, cap), 0);
+            const int lim_lo = max(min(p.causal ? L - p.s_q + 1 + pos_lo : L, cap), 0);
             sg.k_cut = 0x7fffffff;
             if (MIXED && lim_lo != sg.limit) {
                 sg.k_cut = lim_lo / kBlock;   // first tile with tokens past the first row's limit
                 lds_cut[wave][0] = lim_lo;
-                lds_cut[wave][1] = sg.pos_lo;
+                lds_cut[wave][1] = pos_lo;
                 lds_cut[wave][2] = sg.h0;
             }
         }

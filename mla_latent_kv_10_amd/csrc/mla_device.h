@@ -307,8 +307,7 @@ __device__ __forceinline__ f16x4 to_f16x4(float a, float b, float c, float d) {
 
 struct Seg {
     int b, i, h0, limit, t_end, split, n_splits, slot, mask_rows;
-    int pos_lo;  // first position among the unit's rows
-    int k_cut;   // dense: first tile where rows of later positions see more tokens (else INT_MAX)
+    int k_cut;  // dense: first tile where rows of later positions see more tokens (else INT_MAX)
 };
 
 // Row index of token t of tile k (dense): page base from the block table.

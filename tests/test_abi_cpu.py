@@ -267,3 +267,39 @@ def test_static_entry_refuses_shapes_beyond_its_scratch():
     # the workspace fields are ignored: a NULL workspace is not the error reported
     a = _args(workspace=0, workspace_bytes=0, batch=1, s_q=1024, num_parts=256)
     assert L.mla_decode_with_kvcache_static(ctypes.byref(a), None) == m.MLA_ERR_UNSUPPORTED
+
+
+PROBE_MFMA_CASES = [
+    (dict(iters=0), "iters"),
+    (dict(blocks=0), "blocks"),
+    (dict(blocks=(1 << 20) + 1), "blocks"),
+    (dict(sink=0), "sink"),
+    (dict(sink=FAKE + 2), "sink"),
+]
+
+
+@pytest.mark.parametrize("over,text", PROBE_MFMA_CASES)
+def test_mfma_probe_rejects_bad_arguments(over, text):
+    kw = dict(iters=10, blocks=4, sink=FAKE)
+    kw.update(over)
+    assert m.lib().mla_probe_mfma_bf16(kw["iters"], kw["blocks"], 1.0, kw["sink"], None) == m.MLA_ERR_INVALID
+    assert text in m.lib().mla_last_error().decode()
+
+
+PROBE_READ_CASES = [
+    (dict(nbytes=0), "multiple of 16"),
+    (dict(nbytes=24), "multiple of 16"),
+    (dict(blocks=0), "blocks"),
+    (dict(src=0), "non-NULL"),
+    (dict(src=FAKE + 8), "aligned"),
+    (dict(sink=0), "non-NULL"),
+    (dict(sink=FAKE + 1), "aligned"),
+]
+
+
+@pytest.mark.parametrize("over,text", PROBE_READ_CASES)
+def test_read_probe_rejects_bad_arguments(over, text):
+    kw = dict(src=FAKE, nbytes=4096, blocks=4, sink=FAKE)
+    kw.update(over)
+    assert m.lib().mla_probe_hbm_read(kw["src"], kw["nbytes"], kw["blocks"], kw["sink"], None) == m.MLA_ERR_INVALID
+    assert text in m.lib().mla_last_error().decode()
