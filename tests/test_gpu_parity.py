@@ -56,6 +56,9 @@ SMALL = [
                               invalid_frac=0.05)),
     ("bf16 sparse h4 mostly invalid", dict(batch=2, s_q=1, h_q=4, kv_format="bf16", topk=100,
                                            sparse_tokens_per_seq=256, invalid_frac=0.95)),
+    ("bf16 sparse h48 s_q=2", dict(batch=2, s_q=2, h_q=48, kv_format="bf16", topk=300, sparse_tokens_per_seq=1024,
+                                   invalid_frac=0.1)),
+    ("bf16 dense h32 ragged", dict(batch=3, s_q=1, h_q=32, seqlens=[1, 700, 129], kv_format="bf16")),
     ("bf16 sparse prefill chunk h128 s_q=40", dict(batch=2, s_q=40, h_q=128, kv_format="bf16", topk=192,
                                                    sparse_tokens_per_seq=512, prefix_sparse=True)),
     ("fp8 sparse prefill chunk h16 s_q=33", dict(batch=1, s_q=33, h_q=16, kv_format="fp8", topk=100,
