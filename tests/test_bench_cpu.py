@@ -117,3 +117,16 @@ def test_source_hash_ignores_comments_only():
     assert bench.code_without_comments(code) != bench.code_without_comments(code.replace("b;", "c;"))
     assert bench.code_without_comments(code) != bench.code_without_comments(code.replace("// y", "// w"))
     assert bench.code_without_comments("char c = '\\'';  // q\nint d;") == "char c = '\\'';\nint d;"
+
+
+def test_fractions_against_the_measured_peaks():
+    peaks = {"hbm_read_GBps": 7000.0, "mfma_bf16_TFLOPS": 2450.0}
+    out = {"roofline": {"bound": "hbm", "achieved": 3500.0},
+           "sweep": [{"roofline": {"bound": "hbm", "achieved": 700.0}}],
+           "configs": {"a": {"roofline": {"bound": "mfma", "achieved": 980.0}}},
+           "ops": {"q": {"roofline": {"bound": "hbm", "achieved": 1400.0}}}}
+    bench.add_achievable_fracs(out, peaks)
+    assert out["roofline"]["frac_of_achievable"] == 0.5
+    assert out["sweep"][0]["roofline"]["frac_of_achievable"] == 0.1
+    assert out["configs"]["a"]["roofline"]["frac_of_achievable"] == 0.4
+    assert out["ops"]["q"]["roofline"]["frac_of_achievable"] == 0.2

@@ -68,7 +68,7 @@ def test_invariants_random(seed):
 def test_tile_counts_layout():
     # h_q = 128 with 128-row groups, s_q = 2: two row groups per batch entry
     assert tile_counts([64, 65, 0], 3, 2, 128, 0, 128) == [1, 1, 2, 2, 0, 0]
-    # h_q = 20 with 16-row groups: two head blocks
+    # 20 rows cut into 16-row groups: two row blocks (rows 0-15 and 16-19)
     assert tile_counts([130], 1, 1, 20, 0, 16) == [3, 3]
     # sparse ignores cache_seqlens
     assert tile_counts([5, 5], 2, 1, 128, 2048, 128) == [32, 32]
