@@ -15,10 +15,10 @@
 //    each lane names its token's row; a masked token gets an out-of-range
 //    index and the hardware writes zeros, so masked rows are never read.
 //    Two tiles are in flight (double buffering); waits are explicit vmcnt
-//    counts plus raw s_barrier, so prefetches stay outstanding. With 128-head
-//    groups the next tile's loads are spread over the current tile's score
-//    MFMAs: a CU accepts an LDS-direct load only every ~25 cycles, so loads
-//    issued back to back stall the waves issuing them.
+//    counts plus raw s_barrier, so prefetches stay outstanding. With 128-row
+//    groups (and 64-row bf16 groups) the next tile's loads are spread over the
+//    current tile's score MFMAs: a CU accepts an LDS-direct load only every
+//    ~25 cycles, so loads issued back to back stall the waves issuing them.
 //  * The bf16 tile sits in LDS as 72 chunks of 1 KB (8 tokens x 8 16-byte
 //    units), with the unit index XOR-swizzled by (token/2) so that 16 lanes
 //    reading 16 tokens at one unit hit 16 distinct bank groups.
