@@ -291,7 +291,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             return ts;
         };
         // Issue the loads of tile k into LDS region `dst` back to back (the
-        // 64- and 16-head pipelines); returns the tile's validity mask. The
+        // two-tiles-ahead pipeline: 16-row groups, FP8 64-row groups); returns
+        // the tile's validity mask. The
         // number of VMEM instructions per wave is fixed per variant (n_dma).
         // UNROLL: straight-line issue (the prologue).
         auto issue_tile = [&](auto unroll_tag, int k, char LDS_AS* dst, unsigned word) -> uint64_t {
