@@ -236,7 +236,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeParams p) {
             sg.k_cut = 0x7fffffff;
             if (MIXED && lim_lo != sg.limit) {
                 sg.k_cut = lim_lo / kBlock;   // first tile with tokens past the first row's limit
-                lds_cut[wave][0] = lim_lo;
+                // the first row's causal limit before clamping: below 0 when
+                // L < s_q - 1 - pos_lo, so that the rows of positions that see
+                // no token stay fully masked (their limit + offset is <= 0)
+                lds_cut[wave][0] = L - p.s_q + 1 + pos_lo;
                 lds_cut[wave][1] = pos_lo;
                 lds_cut[wave][2] = sg.h0;
             }

@@ -87,6 +87,16 @@ SMALL = [
                                                     causal=True)),
     ("fp8_528 causal s_q=2 h96 packed 192 rows", dict(batch=2, s_q=2, h_q=96, seqlens=[450, 128],
                                                       kv_format="fp8_528", causal=True)),
+    # one head, many positions: every row its own causal limit; with L < s_q the
+    # first rows of the group see no token at all (o = 0, lse = -inf)
+    ("bf16 causal s_q=20 h1 packed", dict(batch=2, s_q=20, h_q=1, seqlens=[300, 129], kv_format="bf16",
+                                          causal=True)),
+    ("fp8 causal s_q=100 h1 packed, L < s_q", dict(batch=2, s_q=100, h_q=1, seqlens=[50, 700], kv_format="fp8",
+                                                   causal=True)),
+    ("bf16 causal s_q=3 h5 packed, L < s_q", dict(batch=3, s_q=3, h_q=5, seqlens=[1, 2, 40], kv_format="bf16",
+                                                  causal=True)),
+    ("fp8_528 causal s_q=4 h12 packed, L < s_q", dict(batch=4, s_q=4, h_q=12, seqlens=[1, 2, 3, 200],
+                                                      kv_format="fp8_528", causal=True)),
     # 528-byte rows: 512-dim keys, 448-dim values, UE8M0 scales per 32 values
     ("fp8_528 dense h128 ragged", dict(batch=3, s_q=1, h_q=128, seqlens=[1, 130, 700], kv_format="fp8_528")),
     ("fp8_528 dense h16 ragged", dict(batch=4, s_q=1, h_q=16, seqlens=[64, 65, 1000, 3], kv_format="fp8_528")),
