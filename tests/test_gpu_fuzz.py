@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _cases(n=32, seed=2024, s_qs=(1, 1, 2, 3), h_qs=(1, 8, 16, 17, 33, 64, 65, 100, 128, 129, 200),
-           fmts=("bf16", "fp8"), modes=("dense", "dense", "causal", "sparse"), tag="fuzz"):
+           fmts=("bf16", "fp8"), modes=("dense", "dense", "causal", "sparse"), tag="fuzz", max_len=700):
     rng = np.random.default_rng(seed)
     out = []
     for k in range(n):
@@ -36,7 +36,7 @@ def _cases(n=32, seed=2024, s_qs=(1, 1, 2, 3), h_qs=(1, 8, 16, 17, 33, 64, 65, 1
             topk = min(topk, tokens - s_q + 1)
             kw.update(topk=topk, sparse_tokens_per_seq=tokens, invalid_frac=float(rng.choice([0.0, 0.05, 0.5])))
         else:
-            lens = rng.integers(0, 700, batch)
+            lens = rng.integers(0, max_len, batch)
             lens[rng.random(batch) < 0.15] = 0
             lens[rng.random(batch) < 0.15] = 1
             kw.update(seqlens=[int(x) for x in lens], causal=(mode == "causal"))
@@ -46,10 +46,14 @@ def _cases(n=32, seed=2024, s_qs=(1, 1, 2, 3), h_qs=(1, 8, 16, 17, 33, 64, 65, 1
 
 
 # the first draw as it always was, then causal-heavy shapes with several query
-# positions (row groups that span positions, every format, 528-byte rows too)
+# positions (row groups that span positions, every format, 528-byte rows too),
+# then causal calls whose sequences are shorter than their query positions
+# (the first positions of a row group see no token)
 CASES = _cases() + _cases(n=24, seed=2026, s_qs=(2, 3, 4), h_qs=(3, 4, 5, 12, 20, 24, 40, 48, 96),
                           fmts=("bf16", "fp8", "fp8_528"), modes=("causal", "causal", "dense", "sparse"),
-                          tag="fuzzpos")
+                          tag="fuzzpos") + \
+    _cases(n=24, seed=2027, s_qs=(3, 5, 8, 13), h_qs=(1, 2, 3, 6, 7, 10, 20, 30), fmts=("bf16", "fp8", "fp8_528"),
+           modes=("causal",), tag="fuzzshort", max_len=24)
 
 
 @pytest.mark.parametrize("label,kw,num_parts", CASES, ids=[c[0] for c in CASES])
