@@ -243,3 +243,29 @@ def test_invalid_page_ids_inside_a_sequence(fmt, h_q):
     assert _same(c, d)
     o_ref, lse_ref = oracle(w)
     compare(d[0], d[1], o_ref, lse_ref, label="positions past the block table", floor_fn=workload_floor_fn(w))
+
+
+@pytest.mark.parametrize("fmt,h_q", [("bf16", 12), ("bf16", 40), ("fp8", 40), ("fp8_528", 12), ("bf16", 128)])
+def test_causal_positions_past_the_block_table(fmt, h_q):
+    """Causal calls with four query positions whose sequences run past their
+    block-table row (3 pages, 192 tokens): position i attends its causal prefix
+    cut at the row's end, so in one row group the early positions end inside
+    the row and the later ones at its end (lengths 193 and 194), all end there
+    (195, 300), or none does (130). Every query row matches the oracle, and
+    widening the row with -1 pages changes nothing."""
+    from tests.gpu_helpers import compare, oracle, workload_floor_fn
+
+    say(f"causal positions past the block table {fmt} h_q={h_q}")
+    lens = [193, 194, 195, 130, 300]
+    w = make_workload(batch=5, s_q=4, h_q=h_q, seqlens=lens, kv_format=fmt, causal=True, extra_blocks=2, seed=33)
+    w.block_table = w.block_table[:, :3].contiguous()
+    a = run_gpu(w)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle(w)
+    compare(a[0], a[1], o_ref, lse_ref, label="causal past the block table", floor_fn=workload_floor_fn(w))
+    # widening the row with pages that name no cache page (-1) leaves the
+    # attended set as it is, and the result the same bit for bit
+    w.block_table = torch.cat([w.block_table, torch.full((5, 2), -1, dtype=torch.int32)], dim=1).contiguous()
+    b_ = run_gpu(w)
+    torch.cuda.synchronize()
+    assert _same(a, b_)
