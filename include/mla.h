@@ -126,19 +126,20 @@ int mla_workspace_size(int batch, int s_q, int h_q, int num_parts, size_t* bytes
 /*
  * Split-KV work schedule ([Walkthrough] §七 "split-KV：把长序列切开":
  * computed once per decode step, reused by every layer).
- *   cache_seqlens  device int32 [batch]; ignored when topk > 0 (may be NULL)
+ *   cache_seqlens  device int32 [batch], 4-byte aligned; ignored when topk > 0
+ *                  (may be NULL)
  *   topk           0 for dense attention, else the sparse index count
  *   num_parts      parts (workgroups) of the decode grid, 1..65535
  *   tile_meta      device int32 [num_parts][8], 16-byte aligned, written: per row
  *                  (placed as above) {q_begin, t_begin, q_end, t_end
  *                  (inclusive), first_split, empty, 0, 0}
- *   split_offsets  device int32 [Q + 1], written: prefix sums of the number
- *                  of splits of each row-group sequence
+ *   split_offsets  device int32 [Q + 1], 4-byte aligned, written: prefix sums
+ *                  of the number of splits of each row-group sequence
  * The result is a pure function of (cache_seqlens, batch, s_q, h_q, topk,
  * num_parts). Reusing it after any of these change gives wrong splits
  * silently; the caller must recompute it ([Walkthrough] §七 warns the same).
- * Errors: MLA_ERR_INVALID for null buffers, batch/s_q/h_q < 1, topk < 0,
- * num_parts out of range; MLA_ERR_UNSUPPORTED if Q > MLA_MAX_UNITS or
+ * Errors: MLA_ERR_INVALID for null or misaligned buffers, batch/s_q/h_q < 1,
+ * topk < 0, num_parts out of range; MLA_ERR_UNSUPPORTED if Q > MLA_MAX_UNITS or
  * topk > MLA_MAX_SEQ_TOKENS.
  */
 int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, int topk,
@@ -147,10 +148,11 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
 typedef struct mla_decode_args {
     int32_t struct_size;       /* must equal sizeof(mla_decode_args) */
     int32_t batch, s_q, h_q;   /* num_heads_k is 1 ([Walkthrough] §六) */
-    const void* q;             /* device bf16 [batch, s_q, h_q, 576]: absorbed latent
-                                  query (512) then rope query (64); 512 dims (448 + 64)
-                                  with MLA_KV_FP8_528 */
-    const void* kv;            /* device uint8 [num_blocks, 64, row_bytes] */
+    const void* q;             /* device bf16 [batch, s_q, h_q, 576], 16-byte aligned:
+                                  absorbed latent query (512) then rope query (64);
+                                  512 dims (448 + 64) with MLA_KV_FP8_528 */
+    const void* kv;            /* device uint8 [num_blocks, 64, row_bytes], 16-byte
+                                  aligned */
     int64_t num_blocks;        /* pages in the cache; num_blocks * 64 * row_bytes
                                   <= 2^32 (4 GiB: rows are addressed with 32-bit
                                   byte offsets from kv) */
@@ -159,13 +161,15 @@ typedef struct mla_decode_args {
                                   MLA_KV_FP8_528; a mismatch is rejected ([Guide]
                                   §"容易踩的坑") */
     int32_t kv_format;         /* MLA_KV_BF16, MLA_KV_FP8_656 or MLA_KV_FP8_528 */
-    const int32_t* block_table;   /* dense: device int32 [batch, max_blocks_per_seq];
-                                     token t of sequence b is row
+    const int32_t* block_table;   /* dense: device int32 [batch, max_blocks_per_seq],
+                                     4-byte aligned; token t of sequence b is row
                                      block_table[b, t/64]*64 + t%64 */
     int32_t max_blocks_per_seq;   /* 1 .. MLA_MAX_SEQ_TOKENS / 64 */
-    const int32_t* cache_seqlens; /* dense: device int32 [batch], tokens per sequence */
-    const int32_t* indices;       /* sparse: device int32 [batch, s_q, topk] absolute
-                                     cache rows (page*64 + offset), -1 = unused
+    const int32_t* cache_seqlens; /* dense: device int32 [batch], 4-byte aligned, tokens
+                                     per sequence */
+    const int32_t* indices;       /* sparse: device int32 [batch, s_q, topk], 4-byte
+                                     aligned: absolute cache rows
+                                     (page*64 + offset), -1 = unused
                                      ([Walkthrough] §八 "当前 master 已经是稀疏注意力");
                                      NULL selects dense attention */
     int32_t topk;              /* sparse: 1 .. MLA_MAX_SEQ_TOKENS, with
@@ -174,14 +178,16 @@ typedef struct mla_decode_args {
     int32_t causal;            /* dense only: query i sees t <= L - s_q + i.
                                   causal with indices -> MLA_ERR_INVALID
                                   ([Guide] §"容易踩的坑") */
-    const int32_t* tile_meta;     /* from mla_get_metadata with the same shapes */
-    const int32_t* split_offsets;
+    const int32_t* tile_meta;     /* from mla_get_metadata with the same shapes;
+                                     16-byte aligned */
+    const int32_t* split_offsets; /* from the same call; 4-byte aligned */
     int32_t num_parts;
     void* workspace;           /* device, >= mla_workspace_size bytes, 256-B aligned */
     size_t workspace_bytes;
     void* o;                   /* device bf16 [batch, s_q, h_q, 512] (448 with
-                                  MLA_KV_FP8_528), written */
-    float* lse;                /* device fp32 [batch, s_q, h_q], written */
+                                  MLA_KV_FP8_528), 16-byte aligned, written */
+    float* lse;                /* device fp32 [batch, s_q, h_q], 4-byte aligned,
+                                  written */
 } mla_decode_args;
 
 /*
@@ -231,8 +237,9 @@ int mla_combine(const mla_decode_args* args, void* stream);
  * scratch: calls that overlap in time on one GPU (other streams, other host
  * threads) race and give wrong results; order them.
  * Errors: those of mla_decode_with_kvcache, plus MLA_ERR_UNSUPPORTED when
- * mla_workspace_size for the call shape exceeds MLA_STATIC_SCRATCH_BYTES
- * (checked on the host before any HIP call).
+ * the split workspace this call needs (the layout under mla_workspace_size
+ * for the call's own kind, dense or sparse) exceeds MLA_STATIC_SCRATCH_BYTES;
+ * that is checked first, on the host, before any HIP call.
  */
 #define MLA_STATIC_SCRATCH_BYTES (64u << 20)
 int mla_decode_with_kvcache_static(const mla_decode_args* args, void* stream);

@@ -108,11 +108,14 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
         if (a->causal) return fail(MLA_ERR_INVALID, "causal masking is not defined with sparse indices");
         if (a->topk > mla::kMaxSeqTokens)
             return fail(MLA_ERR_UNSUPPORTED, "topk must be <= 2^23 (got %d)", a->topk);
+        if (!aligned(a->indices, 4)) return fail(MLA_ERR_INVALID, "indices must be 4-byte aligned");
         if ((int64_t)a->batch * a->s_q * a->topk >= ((int64_t)1 << 29))
             return fail(MLA_ERR_UNSUPPORTED, "batch * s_q * topk must be < 2^29 index entries");
     } else {
         if (!a->block_table || !a->cache_seqlens)
             return fail(MLA_ERR_INVALID, "dense attention needs block_table and cache_seqlens");
+        if (!aligned(a->block_table, 4) || !aligned(a->cache_seqlens, 4))
+            return fail(MLA_ERR_INVALID, "block_table and cache_seqlens must be 4-byte aligned");
         if (a->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID, "max_blocks_per_seq must be >= 1");
         if (a->max_blocks_per_seq > mla::kMaxSeqTokens / mla::kBlock)
             return fail(MLA_ERR_UNSUPPORTED, "max_blocks_per_seq must be <= 2^17 (got %d)", a->max_blocks_per_seq);
@@ -120,6 +123,8 @@ int prepare(const mla_decode_args* a, mla::DecodeParams* p) {
     }
     if (!std::isfinite(a->softmax_scale)) return fail(MLA_ERR_INVALID, "softmax_scale must be finite");
     if (!a->tile_meta || !a->split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
+    if (!aligned(a->tile_meta, 16) || !aligned(a->split_offsets, 4))
+        return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned, split_offsets 4-byte aligned");
     if (!a->workspace) return fail(MLA_ERR_INVALID, "workspace is required");
     if (!aligned(a->workspace, 256)) return fail(MLA_ERR_INVALID, "workspace must be 256-byte aligned");
     const size_t need = workspace_bytes(a->batch, a->s_q, a->h_q, a->num_parts, sparse ? 1 : 0);
@@ -201,8 +206,10 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int s_q, int h_q, 
     if (topk < 0) return fail(MLA_ERR_INVALID, "topk must be >= 0 (got %d)", topk);
     if (topk > mla::kMaxSeqTokens) return fail(MLA_ERR_UNSUPPORTED, "topk must be <= 2^23 (got %d)", topk);
     if (topk == 0 && !cache_seqlens) return fail(MLA_ERR_INVALID, "cache_seqlens is required for dense attention");
+    if (topk == 0 && !aligned(cache_seqlens, 4)) return fail(MLA_ERR_INVALID, "cache_seqlens must be 4-byte aligned");
     if (!tile_meta || !split_offsets) return fail(MLA_ERR_INVALID, "tile_meta and split_offsets are required");
-    if (!aligned(tile_meta, 16)) return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned");
+    if (!aligned(tile_meta, 16) || !aligned(split_offsets, 4))
+        return fail(MLA_ERR_INVALID, "tile_meta must be 16-byte aligned, split_offsets 4-byte aligned");
     const mla::Layout l = mla::layout_for(h_q, s_q, topk > 0);
     mla::MetaParams p;
     p.seqlens = cache_seqlens;

@@ -160,6 +160,14 @@ CASES = [
     (dict(indices=FAKE, topk=(1 << 23) + 1, block_table=0, cache_seqlens=0), m.MLA_ERR_UNSUPPORTED, "2^23"),
     (dict(batch=64, indices=FAKE, topk=1 << 23, block_table=0, cache_seqlens=0), m.MLA_ERR_UNSUPPORTED, "2^29"),
     (dict(max_blocks_per_seq=(1 << 17) + 1), m.MLA_ERR_UNSUPPORTED, "2^17"),
+    (dict(q=FAKE + 8), m.MLA_ERR_INVALID, "aligned"),
+    (dict(kv=FAKE + 4), m.MLA_ERR_INVALID, "aligned"),
+    (dict(lse=FAKE + 2), m.MLA_ERR_INVALID, "aligned"),
+    (dict(tile_meta=FAKE + 4), m.MLA_ERR_INVALID, "tile_meta must be 16-byte aligned"),
+    (dict(split_offsets=FAKE + 2), m.MLA_ERR_INVALID, "split_offsets 4-byte aligned"),
+    (dict(block_table=FAKE + 2), m.MLA_ERR_INVALID, "4-byte aligned"),
+    (dict(cache_seqlens=FAKE + 1), m.MLA_ERR_INVALID, "4-byte aligned"),
+    (dict(indices=FAKE + 2, topk=64, block_table=0, cache_seqlens=0), m.MLA_ERR_INVALID, "indices must be 4-byte"),
 ]
 
 
@@ -188,6 +196,16 @@ def test_null_args_and_metadata_errors():
     assert b"num_parts" in L.mla_last_error()
     assert L.mla_get_metadata(FAKE, 4, 1, 128, (1 << 23) + 1, 256, FAKE, FAKE, None) == m.MLA_ERR_UNSUPPORTED
     assert b"2^23" in L.mla_last_error()
+    # misaligned buffers: a scalar load ignores an address's low bits, so they are refused
+    assert L.mla_get_metadata(FAKE + 2, 4, 1, 128, 0, 256, FAKE, FAKE, None) == m.MLA_ERR_INVALID
+    assert b"cache_seqlens must be 4-byte aligned" in L.mla_last_error()
+    assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 256, FAKE + 8, FAKE, None) == m.MLA_ERR_INVALID
+    assert b"tile_meta must be 16-byte aligned" in L.mla_last_error()
+    assert L.mla_get_metadata(FAKE, 4, 1, 128, 0, 256, FAKE, FAKE + 2, None) == m.MLA_ERR_INVALID
+    assert b"split_offsets 4-byte aligned" in L.mla_last_error()
+    # a sparse call reads no lengths: their pointer is not checked
+    assert L.mla_get_metadata(FAKE + 2, 4, 1, 128, 64, 256, FAKE + 8, FAKE, None) == m.MLA_ERR_INVALID
+    assert b"tile_meta" in L.mla_last_error()
 
 
 QUANT_CASES = [
