@@ -112,6 +112,14 @@ def drain_lib() -> ctypes.CDLL:
 def _load(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing; build it with `python -m mla_latent_kv_10_amd.build`")
+    # One HIP runtime per process. torch, when installed, ships its own
+    # libamdhip64 under the same soname; with torch loaded first this library
+    # binds to that copy. Loaded first, it would bring in the system's copy,
+    # and torch's own would then find no devices.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(path)
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []

@@ -93,3 +93,23 @@ def test_metadata_built_for_another_call_shape_is_refused():
     d["tile_meta"].mla_call_shape = (B, S, H, 0)
     with pytest.raises(ValueError, match="on the GPU"):
         m.make_args(**d)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before anything imports torch, then torch, leaves
+    one HIP runtime in the process (torch's copy), not two."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import mla_latent_kv_10_amd as m\n"
+            "m.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % root
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    paths = eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
