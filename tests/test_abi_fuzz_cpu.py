@@ -197,3 +197,63 @@ def test_one_broken_field_gives_the_documented_status(a, data):
         rc, msg = _call(fn, b)
         assert rc == status, (label, fn.__name__, rc, msg)
         assert msg, (label, fn.__name__)
+
+
+@st.composite
+def valid_metadata_calls(draw):
+    sparse = draw(st.booleans())
+    batch = draw(st.integers(1, 300))
+    s_q = draw(st.integers(1, 64))
+    h_q = draw(st.integers(1, 256))
+    assume(n_row_groups(batch, s_q, h_q, sparse) <= MAX_UNITS)
+    topk = draw(st.integers(1, MAX_SEQ_TOKENS)) if sparse else 0
+    return dict(seqlens=0 if sparse else BASE + 4096, batch=batch, s_q=s_q, h_q=h_q, topk=topk,
+                num_parts=draw(st.integers(1, 65535)), tile_meta=BASE + 8192, split_offsets=BASE + 12288)
+
+
+def _metadata(c):
+    L = m.lib()
+    rc = L.mla_get_metadata(c["seqlens"], c["batch"], c["s_q"], c["h_q"], c["topk"], c["num_parts"],
+                            c["tile_meta"], c["split_offsets"], None)
+    return rc, L.mla_last_error().decode()
+
+
+@SETTINGS
+@given(valid_metadata_calls())
+def test_documented_metadata_calls_pass_validation(c):
+    rc, msg = _metadata(c)
+    assert rc == m.MLA_ERR_HIP, (rc, msg)
+    # the buffer sizes: num_parts rows of 8, and Q + 1 offsets for the larger
+    # Q of the two kinds of call the shape allows
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert m.lib().mla_metadata_size(c["batch"], c["s_q"], c["h_q"], c["num_parts"], ctypes.byref(a),
+                                     ctypes.byref(b)) == m.MLA_OK
+    qs = [n_row_groups(c["batch"], c["s_q"], c["h_q"], sp) for sp in (False, True)]
+    assert a.value == 8 * c["num_parts"]
+    assert b.value == max(q for q in qs if q <= MAX_UNITS) + 1
+
+
+@SETTINGS
+@given(valid_metadata_calls(), st.data())
+def test_metadata_with_one_broken_argument(c, data):
+    per_unit = n_row_groups(1, c["s_q"], c["h_q"], c["topk"] > 0)
+    cases = [
+        ("batch < 1", dict(batch=0), m.MLA_ERR_INVALID),
+        ("s_q < 1", dict(s_q=0), m.MLA_ERR_INVALID),
+        ("h_q < 1", dict(h_q=-2), m.MLA_ERR_INVALID),
+        ("topk < 0", dict(topk=-1), m.MLA_ERR_INVALID),
+        ("topk above 2^23", dict(topk=MAX_SEQ_TOKENS + 1), m.MLA_ERR_UNSUPPORTED),
+        ("num_parts 0", dict(num_parts=0), m.MLA_ERR_INVALID),
+        ("num_parts 65536", dict(num_parts=65536), m.MLA_ERR_INVALID),
+        ("tile_meta NULL", dict(tile_meta=0), m.MLA_ERR_INVALID),
+        ("split_offsets NULL", dict(split_offsets=0), m.MLA_ERR_INVALID),
+        ("tile_meta misaligned", dict(tile_meta=c["tile_meta"] + 4), m.MLA_ERR_INVALID),
+        ("split_offsets misaligned", dict(split_offsets=c["split_offsets"] + 2), m.MLA_ERR_INVALID),
+        ("too many row-group sequences", dict(batch=MAX_UNITS // per_unit + 1), m.MLA_ERR_UNSUPPORTED),
+    ]
+    if c["topk"] == 0:
+        cases += [("cache_seqlens NULL", dict(seqlens=0), m.MLA_ERR_INVALID),
+                  ("cache_seqlens misaligned", dict(seqlens=c["seqlens"] + 2), m.MLA_ERR_INVALID)]
+    label, over, status = data.draw(st.sampled_from(cases), label="mutation")
+    rc, msg = _metadata({**c, **over})
+    assert rc == status and msg, (label, rc, msg)
