@@ -32,6 +32,9 @@
 //    bf16_rne(fp32(e4m3) * fp32 scale) into the bf16 tile once for all waves
 //    ([Guide] §"Crossover" explains the dequant cost; on CDNA4 one workgroup
 //    dequantises a tile once instead of exchanging halves between CTAs).
+//    528-byte rows ([Walkthrough] §八, the V4.1 row) scale each 32 codes by a
+//    power of two (a UE8M0 byte), which gfx950's scaled conversion applies
+//    exactly in the same instruction that widens two codes to bf16.
 //  * The running max is updated lazily: the exponent reference moves only
 //    when a row's max grows by more than 2^8 (exact in real arithmetic; keeps
 //    the O rescale off the common path).
